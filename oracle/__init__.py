@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for video-token attention (dense and block-sparse).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the library or its binding.
+"""
+
+from .attention import (TILE, attention_rows, dense, keep_count, kept_keys, select_tiles,
+                        sparse, tile_count, tile_means, tile_scores, top_tiles)
+from .widen import widen
+
+__all__ = ["TILE", "attention_rows", "dense", "keep_count", "kept_keys", "select_tiles",
+           "sparse", "tile_count", "tile_means", "tile_scores", "top_tiles", "widen"]

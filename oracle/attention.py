@@ -1,0 +1,184 @@
+"""fp64 CPU oracle for dense and block-sparse video-token attention.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this module.  It shares no code with
+the HIP library and imports nothing from it.
+
+Inputs are the exact bfloat16 values widened to float64 (exact).  Everything is
+plain numpy: a matmul serves as a step of the dense definition, nothing else is
+blocked, fused or reordered.
+
+Sources (the pages are the authority on what is computed):
+
+* Dense attention: the joint attention of MiniMax H3 is one bidirectional
+  (non-causal) softmax attention over the packed token sequence (FastH3 page,
+  "FastH3 Preview v1: four calls, one-tenth the attention...", section "Lever
+  two: VSA-H3 makes each of the four calls cheaper"); scores are streamed, never
+  materialized (FreeVideo page, section "Why it does not fit: the arithmetic").
+  The oracle is the plain definition, softmax(scale * Q K^T) V.
+* Tile selection: a coarse pooling stage scores every tile against the query
+  tile, then ``compute_topk`` keeps max(1, min(ceil((1 - sparsity) * blocks),
+  blocks)) tiles (FastH3 page, "Lever two").  The pages do not fix the pooling
+  operator, the score precision or the tie rule; the readings used here are:
+  mean over the valid tokens of a contiguous 128-token tile, fp64 sums in token
+  order, one correctly rounded division, an unscaled fp64 dot product summed in
+  order d = 0..127 with every product and every sum rounded (no fused
+  multiply-add), the k largest scores with ties going to the lower tile index,
+  emitted in ascending tile order.
+* Sparse attention: exact attention restricted to the kept tiles, with the
+  compression branch contributing nothing, which is the base-weight behaviour
+  (FastH3 page, "Lever two": the base loader zero-initializes
+  ``to_gate_compress``).  Softmax is normalized over the kept keys only.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TILE = 128
+
+
+# --------------------------------------------------------------------------
+# dense attention (definition)
+# --------------------------------------------------------------------------
+
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * q k^T) v for a block of query rows of one head.
+
+    q: [R, d]; k, v: [N, d], all float64.  Returns [R, d] float64.
+    Non-causal: every query sees every key.
+    """
+    s = scale * (q @ k.T)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ v) / l
+
+
+def dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, rows=None,
+          block: int = 256) -> np.ndarray:
+    """Dense attention of every head.
+
+    q, k, v: [H, N, d] float64.  ``rows`` (optional) is a 1-D index array of
+    query rows to compute (the same rows for every head); the result is then
+    [H, len(rows), d].
+    """
+    H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.empty((H, len(rows), d), dtype=np.float64)
+    for h in range(H):
+        for b in range(0, len(rows), block):
+            r = rows[b:b + block]
+            out[h, b:b + len(r)] = attention_rows(q[h, r], k[h], v[h], scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# tile selection (algorithm, in the order the FastH3 page gives it:
+# coarse pooled scores first, then compute_topk decides how many survive)
+# --------------------------------------------------------------------------
+
+def tile_count(tokens: int) -> int:
+    """Number of contiguous 128-token tiles covering ``tokens`` tokens."""
+    return -(-tokens // TILE)
+
+
+def keep_count(num_tiles: int, keep_frac: float) -> int:
+    """compute_topk's rule with keep_frac = 1 - sparsity, in IEEE double.
+
+    A sequence with no tiles keeps none.
+    """
+    if num_tiles == 0:
+        return 0
+    return max(1, min(math.ceil(keep_frac * num_tiles), num_tiles))
+
+
+def tile_means(x: np.ndarray) -> np.ndarray:
+    """Mean of each tile's valid tokens, for one head.
+
+    x: [N, d] float64.  Returns [T, d] float64.  Each tile sum runs in token
+    order starting from +0.0; the mean is one correctly rounded division by the
+    number of valid tokens in the tile.
+    """
+    N, d = x.shape
+    T = tile_count(N)
+    starts = np.arange(T) * TILE
+    counts = np.minimum(starts + TILE, N) - starts
+    acc = np.zeros((T, d), dtype=np.float64)
+    for i in range(TILE):          # i-th token of every tile, in token order
+        live = i < counts
+        acc[live] = acc[live] + x[starts[live] + i]
+    return acc / counts[:, None].astype(np.float64)
+
+
+def tile_scores(qm: np.ndarray, km: np.ndarray) -> np.ndarray:
+    """sigma[i, j] = sum_d qm[i, d] * km[j, d] (unscaled), for one head.
+
+    qm: [T, d], km: [T, d] float64.  The sum starts at +0.0 and runs d = 0..d-1;
+    every product and every sum is one IEEE double rounding (separate numpy
+    multiply and add, no fused multiply-add).
+    """
+    T, d = qm.shape
+    acc = np.zeros((T, km.shape[0]), dtype=np.float64)
+    for c in range(d):
+        acc = acc + np.multiply.outer(qm[:, c], km[:, c])
+    return acc
+
+
+def top_tiles(sigma: np.ndarray, k: int) -> np.ndarray:
+    """Per row, the k largest scores (ties -> lower column), ascending.
+
+    sigma: [T, T] float64.  Returns int32 [T, k].
+    """
+    T = sigma.shape[0]
+    out = np.empty((T, k), dtype=np.int32)
+    for i in range(T):
+        order = np.argsort(-sigma[i], kind="stable")  # descending, stable on ties
+        out[i] = np.sort(order[:k])
+    return out
+
+
+def select_tiles(q: np.ndarray, k: np.ndarray, keep_frac: float) -> np.ndarray:
+    """Tile indices kept for every head and query tile.
+
+    q, k: [H, N, d] float64.  Returns int32 [H, T, kk] with kk = keep_count(T, keep_frac).
+    """
+    H, N, _ = q.shape
+    T = tile_count(N)
+    kk = keep_count(T, keep_frac)
+    out = np.empty((H, T, kk), dtype=np.int32)
+    for h in range(H):
+        sigma = tile_scores(tile_means(q[h]), tile_means(k[h]))
+        out[h] = top_tiles(sigma, kk)
+    return out
+
+
+# --------------------------------------------------------------------------
+# sparse attention (exact attention over the kept tiles only)
+# --------------------------------------------------------------------------
+
+def kept_keys(tiles, tokens: int) -> np.ndarray:
+    """Token indices of the given tiles (valid tokens only), tile order kept."""
+    return np.concatenate([np.arange(t * TILE, min(t * TILE + TILE, tokens)) for t in tiles])
+
+
+def sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, idx: np.ndarray,
+           rows=None) -> np.ndarray:
+    """Block-sparse attention: query i of tile t sees only the tokens of tiles idx[h, t].
+
+    q, k, v: [H, N, d] float64; idx: int [H, T, kk].  ``rows`` as in ``dense``.
+    """
+    H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    out = np.empty((H, len(rows), d), dtype=np.float64)
+    tile_of = rows // TILE
+    for h in range(H):
+        for t in np.unique(tile_of):
+            sel = np.nonzero(tile_of == t)[0]
+            keys = kept_keys(idx[h, t], N)
+            out[h, sel] = attention_rows(q[h, rows[sel]], k[h, keys], v[h, keys], scale)
+    return out
