@@ -1,0 +1,149 @@
+/*
+ * fvattn.h - C ABI of the MI355X (gfx950) video-token attention library.
+ *
+ * What is computed
+ * ----------------
+ * Multi-head softmax attention over the packed video-token sequence of a
+ * MiniMax-H3-shaped denoiser: 56 heads of width 128, 1,008 tokens per latent
+ * frame (FreeVideo page "FreeVideo: a 66 GB video transformer on an 8 GB
+ * card...", section "What MiniMax H3 is, briefly").  The attention is one
+ * bidirectional (non-causal) softmax attention (FastH3 page "FastH3 Preview v1:
+ * four calls, one-tenth the attention...", section "Lever two: VSA-H3 makes
+ * each of the four calls cheaper"), streamed so that the score matrix is never
+ * materialized (FreeVideo page, section "Why it does not fit: the
+ * arithmetic").
+ *
+ * Two modes:
+ *   FVATTN_DENSE         out = softmax(scale * Q K^T) V over every key.
+ *   FVATTN_BLOCK_SPARSE  the sequence is cut into contiguous 128-token tiles;
+ *                        tiles are mean-pooled, every query tile scores every
+ *                        key tile with the pooled dot product, the top
+ *                        k = max(1, min(ceil(keep_frac * T), T)) key tiles are
+ *                        kept (compute_topk, FastH3 page, "Lever two"), and
+ *                        exact attention runs over the kept tiles only, the
+ *                        softmax normalized over the kept keys.
+ *
+ * Selection rule, exactly (the pages leave these points open; this is the
+ * library's definition): tile t covers tokens [128t, min(128t+128, N)) and has
+ * n_t valid tokens; its mean is an fp64 sum in token order starting from +0.0
+ * followed by one correctly rounded fp64 division by n_t; the score of (query
+ * tile i, key tile j) is the unscaled fp64 dot product of the two means summed
+ * from +0.0 in order d = 0..127 with every product and every sum rounded
+ * separately (no fused multiply-add); a query tile keeps the k highest scores,
+ * ties going to the lower key-tile index; kept indices are listed ascending.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Layout: q, k, v and out are contiguous bfloat16 arrays [heads][tokens][128]
+ *   (head-major), device pointers.  A head group is therefore a contiguous
+ *   sub-array.  Index arrays are int32 [heads][T][k], T = ceil(tokens/128),
+ *   device pointers, ascending within each row.
+ * Ownership: the caller owns every buffer and the stream.  The library never
+ *   frees caller memory.  Sparse mode allocates its scratch (tile means and
+ *   index lists) stream-ordered on the caller's stream and releases it there.
+ * Stream: `stream` is a hipStream_t passed as void*; NULL means the default
+ *   stream.  Every call only enqueues work and returns; no host
+ *   synchronization happens inside.
+ * Bounds: nothing is read or written past `tokens`; a partial last tile is
+ *   masked (its missing keys get -inf scores, its missing query rows are never
+ *   stored).
+ * Empty input: heads == 0 or tokens == 0 is a valid call that does nothing.
+ * Errors: arguments are checked on the host before any HIP call, and a failing
+ *   check launches nothing.  No call aborts, throws or prints.  Status codes:
+ *     FVATTN_ERR_INVALID_ARG  a NULL pointer, heads < 0, tokens < 0, a scale
+ *                             that is not finite and > 0, an unknown mode, a
+ *                             keep_frac that is NaN or outside (0, 1] (sparse
+ *                             only; ignored in dense mode), keep outside [1, T].
+ *     FVATTN_ERR_UNSUPPORTED  head_dim != 128, group_heads not in {16, 8, 4},
+ *                             sparse mode with T > FVATTN_MAX_TILES, a tensor
+ *                             with 2^31 or more elements, or a current device
+ *                             that is not gfx950.
+ *     FVATTN_ERR_ALLOC        a stream-ordered scratch allocation failed.
+ *     FVATTN_ERR_HIP          a HIP call or kernel launch reported an error.
+ * Numerics: QK^T and PV run as bf16 matrix-core products with fp32
+ *   accumulation; the online softmax keeps an fp32 running max and sum; P is
+ *   rounded to bf16 before the PV product; out is rounded to bf16.
+ */
+#ifndef FVATTN_H
+#define FVATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FVATTN_OK = 0,
+  FVATTN_ERR_INVALID_ARG = 1,
+  FVATTN_ERR_UNSUPPORTED = 2,
+  FVATTN_ERR_ALLOC = 3,
+  FVATTN_ERR_HIP = 4
+} fvattn_status;
+
+typedef enum { FVATTN_DENSE = 0, FVATTN_BLOCK_SPARSE = 1 } fvattn_mode;
+
+#define FVATTN_TILE 128       /* tokens per selection tile */
+#define FVATTN_HEAD_DIM 128   /* the only supported head width */
+#define FVATTN_MAX_TILES 2048 /* sparse mode: at most 2048 tiles (262,144 tokens) */
+
+/* Keep count of compute_topk (FastH3 page, "Lever two"):
+ * k = max(1, min(ceil(keep_frac * T), T)) with T = ceil(tokens / 128), the
+ * product taken in IEEE double.  tokens == 0 gives 0.  Returns k >= 0, or
+ * -FVATTN_ERR_INVALID_ARG for tokens < 0 or keep_frac NaN or outside (0, 1].
+ * Pure host arithmetic. */
+int fvattn_keep_count(int tokens, double keep_frac);
+
+/* Attention forward for `heads` heads of `tokens` tokens (see the header
+ * comment for the two modes).  q, k, v: bf16 [heads][tokens][head_dim] in;
+ * out: bf16 [heads][tokens][head_dim] out (every row written).  scale
+ * multiplies QK^T (1/sqrt(128) for H3-shaped heads).  keep_frac is used in
+ * FVATTN_BLOCK_SPARSE mode only. */
+int fvattn_forward(const void* q, const void* k, const void* v, void* out, int heads, int tokens,
+                   int head_dim, float scale, int mode, double keep_frac, void* stream);
+
+/* The selection of FVATTN_BLOCK_SPARSE mode alone (the coarse pooled-score
+ * stage and compute_topk of FastH3 page, "Lever two").  q, k: bf16
+ * [heads][tokens][head_dim] in; idx_out: int32 [heads][T][k] out, with
+ * k = fvattn_keep_count(tokens, keep_frac), ascending per row. */
+int fvattn_select_tiles(const void* q, const void* k, int heads, int tokens, int head_dim,
+                        double keep_frac, int32_t* idx_out, void* stream);
+
+/* Sparse attention from caller-given tile lists (the role of
+ * block_sparse_attn_from_indices on the FastH3 page, section "What's actually
+ * on the GPU: three kernels behind one switch").  idx: int32 [heads][T][keep]
+ * in, every entry in [0, T), ascending and distinct within a row (not checked
+ * on the device: an out-of-range entry is clamped to T-1 and a repeated one is
+ * attended twice).  keep in [1, T]. */
+int fvattn_forward_indexed(const void* q, const void* k, const void* v, const int32_t* idx,
+                           int keep, void* out, int heads, int tokens, int head_dim, float scale,
+                           void* stream);
+
+/* Head-group launcher: runs fvattn_forward on consecutive groups of
+ * group_heads heads (16, 8 or 4), the last group taking the remainder (56 in
+ * groups of 16 is 16+16+16+8), in order on the one stream.  This mirrors the
+ * planner's head grouping (FreeVideo page, section "The rest is placement",
+ * item 1; FreeVideo Adaptive Execution Planner page, section "Plan", row
+ * "Attention").  Arguments as fvattn_forward with total_heads heads. */
+int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out, int total_heads,
+                         int group_heads, int tokens, int head_dim, float scale, int mode,
+                         double keep_frac, void* stream);
+
+/* Step S1 alone, for checking: fp64 tile means of x, bf16 [heads][tokens][128]
+ * in, means_out fp64 [heads][T][128] out (device pointers). */
+int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double* means_out,
+                      void* stream);
+
+/* Step S2 alone, for checking: fp64 scores [heads][T][T] of the tile means
+ * qm, km (fp64 [heads][T][128], device pointers) by the canonical rule. */
+int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles, int head_dim,
+                       double* scores_out, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* fvattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FVATTN_H */

@@ -1,0 +1,170 @@
+"""Host-side tests of the C ABI: the library loads, exports what include/fvattn.h
+declares, and checks its arguments on the host.  No compute runs here."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_amd as fv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fvattn.h")
+
+# never dereferenced: every call below fails its host checks first
+BOGUS = ctypes.c_void_p(0x1000)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fvattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fv.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fv.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for s in range(0, 6):
+        assert fv.status_string(s)
+    assert "INVALID" in fv.status_string(fv.FVATTN_ERR_INVALID_ARG)
+    assert "unknown" in fv.status_string(99)
+
+
+def test_keep_count_matches_oracle(lib):
+    for tokens in [1, 127, 128, 129, 1008, 5040, 72576, 102816, 262144, 300000]:
+        for f in [1e-9, 0.01, 0.07, 0.1, 1 - 0.9, 0.14, 0.25, 0.3, 0.5, 0.99, 1.0]:
+            T = oracle.tile_count(tokens)
+            assert fv.keep_count(tokens, f) == oracle.keep_count(T, f), (tokens, f)
+    assert fv.keep_count(72576, 0.1) == 57
+    assert fv.keep_count(102816, 0.1) == 81
+    assert fv.keep_count(0, 0.1) == 0
+
+
+@pytest.mark.parametrize("frac", [0.0, -0.1, 1.5, float("nan"), float("inf")])
+def test_keep_count_rejects_bad_fraction(lib, frac):
+    assert lib.fvattn_keep_count(1008, frac) == -fv.FVATTN_ERR_INVALID_ARG
+
+
+def test_keep_count_rejects_negative_tokens(lib):
+    assert lib.fvattn_keep_count(-1, 0.1) == -fv.FVATTN_ERR_INVALID_ARG
+
+
+def _fwd(lib, q=BOGUS, k=BOGUS, v=BOGUS, o=BOGUS, heads=4, tokens=1008, hd=128, scale=0.088,
+         mode=0, frac=0.1):
+    return lib.fvattn_forward(q, k, v, o, heads, tokens, hd, scale, mode, frac, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(k=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(v=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(o=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(heads=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(tokens=-5), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(hd=64), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(hd=256), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=7), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=1, frac=0.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=1, frac=1.01), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=1, frac=float("nan")), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(mode=1, tokens=2048 * 128 + 1), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(tokens=(1 << 31) // 128 + 1), fv.FVATTN_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_bad_arguments(lib, kw, want):
+    assert _fwd(lib, **kw) == want
+
+
+def test_dense_ignores_keep_frac_checks(lib):
+    # keep_frac is not looked at in dense mode: a bad one plus a NULL pointer
+    # still reports the pointer
+    assert _fwd(lib, q=NULL, frac=float("nan")) == fv.FVATTN_ERR_INVALID_ARG
+
+
+def test_empty_inputs_are_noops(lib):
+    # nothing to do: OK without touching any pointer or the device
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0) == fv.FVATTN_OK
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, heads=0) == fv.FVATTN_OK
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0, mode=1) == fv.FVATTN_OK
+    assert lib.fvattn_select_tiles(NULL, NULL, 0, 1008, 128, 0.1, NULL, NULL) == fv.FVATTN_OK
+    assert lib.fvattn_forward_indexed(NULL, NULL, NULL, NULL, 1, NULL, 4, 0, 128, 0.1, NULL) == 0
+    assert lib.fvattn_forward_heads(NULL, NULL, NULL, NULL, 0, 16, 1008, 128, 0.1, 0, 0.1, NULL) == 0
+    assert lib.fvattn_tile_means(NULL, 0, 10, 128, NULL, NULL) == fv.FVATTN_OK
+    assert lib.fvattn_tile_scores(NULL, NULL, 3, 0, 128, NULL, NULL) == fv.FVATTN_OK
+
+
+def test_select_tiles_rejects_bad_arguments(lib):
+    st = lib.fvattn_select_tiles
+    assert st(NULL, BOGUS, 4, 1008, 128, 0.1, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert st(BOGUS, BOGUS, 4, 1008, 128, 0.1, NULL, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert st(BOGUS, BOGUS, 4, 1008, 128, 0.0, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert st(BOGUS, BOGUS, 4, 1008, 120, 0.1, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert st(BOGUS, BOGUS, 4, 2049 * 128, 128, 0.1, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert st(BOGUS, BOGUS, -4, 1008, 128, 0.1, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
+def test_forward_indexed_rejects_bad_keep(lib):
+    fi = lib.fvattn_forward_indexed
+    # 1008 tokens = 8 tiles: keep must be in [1, 8]
+    assert fi(BOGUS, BOGUS, BOGUS, BOGUS, 0, BOGUS, 4, 1008, 128, 0.1, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fi(BOGUS, BOGUS, BOGUS, BOGUS, 9, BOGUS, 4, 1008, 128, 0.1, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fi(BOGUS, BOGUS, BOGUS, NULL, 2, BOGUS, 4, 1008, 128, 0.1, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fi(BOGUS, BOGUS, BOGUS, BOGUS, 2, BOGUS, 4, 1008, 128, 0.0, NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("group", [0, 1, 2, 3, 5, 12, 32, 56])
+def test_forward_heads_rejects_bad_group(lib, group):
+    assert lib.fvattn_forward_heads(BOGUS, BOGUS, BOGUS, BOGUS, 56, group, 1008, 128, 0.088, 0, 0.1,
+                                    NULL) == fv.FVATTN_ERR_UNSUPPORTED
+
+
+def test_tile_scores_rejects_bad_arguments(lib):
+    ts = lib.fvattn_tile_scores
+    assert ts(NULL, BOGUS, 2, 8, 128, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert ts(BOGUS, BOGUS, 2, 8, 64, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert ts(BOGUS, BOGUS, 2, 4096, 128, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+
+
+def test_alloc_failure_hook_launches_nothing(lib, monkeypatch):
+    monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
+    assert _fwd(lib, mode=1) == fv.FVATTN_ERR_ALLOC
+    assert lib.fvattn_select_tiles(BOGUS, BOGUS, 4, 1008, 128, 0.1, BOGUS, NULL) == fv.FVATTN_ERR_ALLOC
+    assert lib.fvattn_forward_heads(BOGUS, BOGUS, BOGUS, BOGUS, 56, 16, 1008, 128, 0.088, 1, 0.1,
+                                    NULL) == fv.FVATTN_ERR_ALLOC
+    assert lib.fvattn_tile_scores(BOGUS, BOGUS, 2, 8, 128, BOGUS, NULL) == fv.FVATTN_ERR_ALLOC
+    # argument errors still come first
+    assert _fwd(lib, mode=1, q=NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful on a host without a GPU")
+def test_no_device_reports_hip_error(lib):
+    # valid arguments but no GPU: the device check fails before any launch
+    assert _fwd(lib) == fv.FVATTN_ERR_HIP
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fv.forward(q, q, q)
+    with pytest.raises(TypeError):
+        fv.forward(q.float(), q.float(), q.float())

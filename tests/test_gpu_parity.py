@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: selected tile indices bit-exact; tile means and tile scores bit-exact;
+attention outputs within max-abs 2e-2 and mean-abs 2e-3 of the oracle over all
+compared elements.  Small shapes are compared in full; the full-size workloads
+(72,576 and 102,816 tokens) on sampled query rows, with the selection compared
+in full.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_amd as fv
+from video_diffusion_transformer_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[parity]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    say(f"{what}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_fro={rel:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (what, mx, mean)
+
+
+def sample_rows(N, n_random, seed):
+    rng = np.random.default_rng(seed)
+    T = oracle.tile_count(N)
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, (T - 1) * 128, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(rng.integers(0, N, n_random).tolist())
+    return np.array(sorted(rows))
+
+
+# ------------------------------------------------------------------ dense
+
+@pytest.mark.parametrize("N", [1, 5, 63, 64, 65, 127, 128, 129, 200, 300, 1000, 1008])
+def test_dense_small_shapes_full(N):
+    say("dense small N=", N)
+    q, k, v = inputs.make_qkv(N, 2, "iid", 100 + N)
+    out = fv.forward(*to_dev(q, k, v)).cpu()
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128))
+    assert_close(oracle.widen(out), ref, f"dense N={N}")
+
+
+def test_dense_config1_full():
+    c = inputs.CONFIGS[1]
+    say("dense config", c.name)
+    q, k, v = inputs.make_inputs(1)
+    out = fv.forward(*to_dev(q, k, v), scale=c.scale).cpu()
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), c.scale)
+    assert_close(oracle.widen(out), ref, c.name)
+
+
+def test_dense_config2_56_heads():
+    c = inputs.CONFIGS[2]
+    say("dense config", c.name)
+    q, k, v = inputs.make_inputs(2)
+    out = fv.forward(*to_dev(q, k, v), scale=c.scale).cpu()
+    # 8 heads in full, the rest on sampled rows
+    full = oracle.dense(*(oracle.widen(t[:8]) for t in (q, k, v)), c.scale)
+    assert_close(oracle.widen(out[:8]), full, c.name + " heads 0-7 full")
+    rows = sample_rows(c.tokens, 48, 2)
+    ref = oracle.dense(*(oracle.widen(t[8:]) for t in (q, k, v)), c.scale, rows=rows)
+    assert_close(oracle.widen(out[8:, rows]), ref, c.name + " heads 8-55 sampled")
+
+
+def test_dense_frame_correlated_small():
+    say("dense frame-correlated 3 frames")
+    q, k, v = inputs.make_qkv(3024, 3, "frame", 7)
+    out = fv.forward(*to_dev(q, k, v)).cpu()
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128))
+    assert_close(oracle.widen(out), ref, "frame 3024")
+
+
+def test_dense_on_side_stream_and_scale():
+    q, k, v = inputs.make_qkv(700, 2, "iid", 9)
+    s = torch.cuda.Stream(device=DEV)
+    qd, kd, vd = to_dev(q, k, v)
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(s):
+        out = fv.forward(qd, kd, vd, scale=0.3, stream=s)
+    s.synchronize()
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), 0.3)
+    assert_close(oracle.widen(out.cpu()), ref, "side stream scale 0.3")
+
+
+def test_dense_writes_nothing_past_the_output():
+    N, H = 300, 2
+    q, k, v = to_dev(*inputs.make_qkv(N, H, "iid", 11))
+    n = H * N * 128
+    buf = torch.full((n + 4096,), 12345.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[:n].view(H, N, 128)
+    fv.forward(q, k, v, out=out)
+    tail = buf[n:].cpu()
+    assert torch.all(tail == 12345.0)
+
+
+# ------------------------------------------------------------------ selection steps
+
+@pytest.mark.parametrize("N", [1, 100, 128, 300, 1008, 5040])
+def test_tile_means_bit_exact(N):
+    x = inputs.make_qkv(N, 3, "frame", 20 + N)[0]
+    got = fv.tile_means(x.to(DEV)).cpu().numpy()
+    ref = np.stack([oracle.tile_means(oracle.widen(x[h])) for h in range(3)])
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("T", [1, 7, 40, 567])
+def test_tile_scores_bit_exact(T):
+    rng = np.random.default_rng(T)
+    qm = rng.standard_normal((2, T, 128))
+    km = rng.standard_normal((2, T, 128))
+    got = fv.tile_scores(torch.from_numpy(qm).to(DEV), torch.from_numpy(km).to(DEV)).cpu().numpy()
+    ref = np.stack([oracle.tile_scores(qm[h], km[h]) for h in range(2)])
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("N,frac,dist", [(1008, 0.1, "iid"), (1000, 0.3, "iid"), (5040, 0.1, "frame"),
+                                         (5040, 0.25, "iid"), (20000, 0.1, "frame"),
+                                         (129, 0.5, "iid"), (1, 0.1, "iid"), (3000, 1.0, "frame")])
+def test_select_tiles_bit_exact_small(N, frac, dist):
+    say("select", N, frac, dist)
+    q, k, _ = inputs.make_qkv(N, 3, dist, 30 + N)
+    got = fv.select_tiles(*to_dev(q, k), keep_frac=frac).cpu().numpy()
+    ref = oracle.select_tiles(oracle.widen(q), oracle.widen(k), frac)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_select_zero_queries_take_lowest_tiles():
+    N = 3000
+    q = torch.zeros((2, N, 128), dtype=torch.bfloat16)
+    k = inputs.make_qkv(N, 2, "iid", 3)[1]
+    got = fv.select_tiles(*to_dev(q, k), keep_frac=0.2).cpu().numpy()
+    kk = oracle.keep_count(oracle.tile_count(N), 0.2)
+    assert np.array_equal(got, np.broadcast_to(np.arange(kk, dtype=np.int32), got.shape))
+
+
+def test_select_ties_exact_on_tile_constant_inputs():
+    # tile j of K is the constant j in channel 0 -> scores q0 * j, with exact ties
+    # between the tiles of equal value
+    N, d = 2000, 128
+    k = torch.zeros((1, N, d))
+    k[0, :, 0] = torch.div(torch.arange(N), 128, rounding_mode="floor") % 4
+    q = torch.zeros((1, N, d))
+    q[0, :, 0] = 1.0
+    q[0, 512:640, 0] = -1.0
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    got = fv.select_tiles(*to_dev(qb, kb), keep_frac=0.3).cpu().numpy()
+    ref = oracle.select_tiles(oracle.widen(qb), oracle.widen(kb), 0.3)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ sparse
+
+@pytest.mark.parametrize("N,keep", [(300, 1), (300, 2), (1008, 3), (1000, 8), (2080, 5), (129, 1)])
+def test_forward_indexed_matches_oracle(N, keep):
+    say("indexed", N, keep)
+    H = 2
+    q, k, v = inputs.make_qkv(N, H, "iid", 40 + N)
+    T = oracle.tile_count(N)
+    rng = np.random.default_rng(N + keep)
+    idx = np.stack([np.stack([np.sort(rng.choice(T, keep, replace=False)) for _ in range(T)])
+                    for _ in range(H)]).astype(np.int32)
+    idx[0, 0] = np.arange(T - keep, T)   # make sure the partial last tile is used
+    out = fv.forward_indexed(*to_dev(q, k, v), torch.from_numpy(idx).to(DEV)).cpu()
+    ref = oracle.sparse(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128), idx)
+    assert_close(oracle.widen(out), ref, f"indexed N={N} keep={keep}")
+
+
+@pytest.mark.parametrize("N,frac", [(1008, 0.1), (1000, 0.3), (5040, 0.1), (20000, 0.1)])
+def test_sparse_forward_matches_oracle(N, frac):
+    say("sparse", N, frac)
+    q, k, v = inputs.make_qkv(N, 2, "frame", 50 + N)
+    out = fv.forward(*to_dev(q, k, v), mode="sparse", keep_frac=frac).cpu()
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    idx = oracle.select_tiles(qw, kw, frac)
+    rows = None if N <= 5040 else sample_rows(N, 200, 5)
+    ref = oracle.sparse(qw, kw, vw, 1 / math.sqrt(128), idx, rows=rows)
+    got = oracle.widen(out) if rows is None else oracle.widen(out[:, rows])
+    assert_close(got, ref, f"sparse N={N} keep_frac={frac}")
+
+
+@pytest.mark.parametrize("N", [1008, 1000, 129, 64])
+def test_sparse_keep_all_is_dense_bitwise(N):
+    q, k, v = to_dev(*inputs.make_qkv(N, 2, "iid", 60 + N))
+    a = fv.forward(q, k, v, mode="sparse", keep_frac=1.0)
+    b = fv.forward(q, k, v, mode="dense")
+    assert torch.equal(a, b)
+
+
+def test_head_groups_equal_one_launch_bitwise():
+    q, k, v = to_dev(*inputs.make_qkv(1500, 12, "frame", 70))
+    for mode in ("dense", "sparse"):
+        whole = fv.forward(q, k, v, mode=mode, keep_frac=0.25)
+        for g in (16, 8, 4):
+            grouped = fv.forward_heads(q, k, v, g, mode=mode, keep_frac=0.25)
+            assert torch.equal(whole, grouped), (mode, g)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.fixture(scope="module")
+def cfg4():
+    say("generating 72,576 x 56 frame-correlated inputs")
+    return inputs.make_inputs(4)
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    say("generating 102,816 x 56 frame-correlated inputs")
+    return inputs.make_inputs(5)
+
+
+def test_config3_dense_sampled():
+    c = inputs.CONFIGS[3]
+    say("config", c.name)
+    q, k, v = inputs.make_inputs(3)
+    out = fv.forward_heads(*to_dev(q, k, v), c.group, scale=c.scale).cpu()
+    rows = sample_rows(c.tokens, 40, 3)
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), c.scale, rows=rows)
+    assert_close(oracle.widen(out[:, rows]), ref, c.name)
+
+
+def _full_size_sparse_and_dense(cid, qkv):
+    c = inputs.CONFIGS[cid]
+    q, k, v = qkv
+    qd, kd, vd = to_dev(q, k, v)
+    say(c.name, "selection")
+    idx = fv.select_tiles(qd, kd, keep_frac=c.keep_frac).cpu().numpy()
+    T = oracle.tile_count(c.tokens)
+    assert idx.shape == (c.heads, T, oracle.keep_count(T, c.keep_frac))
+    for h in range(c.heads):
+        ref = oracle.select_tiles(oracle.widen(q[h:h + 1]), oracle.widen(k[h:h + 1]), c.keep_frac)
+        assert np.array_equal(idx[h:h + 1], ref), h
+    say(c.name, "selection bit-exact for all heads")
+    rows = sample_rows(c.tokens, 24, cid)
+    heads = list(range(0, c.heads, 5)) + [c.heads - 1]
+    for mode in ("sparse", "dense"):
+        out = fv.forward_heads(qd, kd, vd, c.group, scale=c.scale, mode=mode, keep_frac=c.keep_frac)
+        got = out[heads][:, rows].cpu()
+        qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
+        if mode == "sparse":
+            ref = oracle.sparse(qw, kw, vw, c.scale, idx[heads], rows=rows)
+        else:
+            ref = oracle.dense(qw, kw, vw, c.scale, rows=rows)
+        assert_close(oracle.widen(got), ref, f"{c.name} {mode}")
+        del out
+
+
+def test_config4_sparse_and_dense(cfg4):
+    _full_size_sparse_and_dense(4, cfg4)
+
+
+def test_config5_sparse_and_dense(cfg5):
+    _full_size_sparse_and_dense(5, cfg5)

@@ -1,1 +1,210 @@
-"""MI355X (gfx950) dense and block-sparse attention over video tokens."""
+"""MI355X (gfx950) dense and block-sparse attention over video tokens.
+
+A thin ctypes binding of the C ABI in include/fvattn.h, with the same names.
+It only marshals arguments: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if libfvattn.so is missing or fails to load,
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfvattn.so")
+
+FVATTN_OK = 0
+FVATTN_ERR_INVALID_ARG = 1
+FVATTN_ERR_UNSUPPORTED = 2
+FVATTN_ERR_ALLOC = 3
+FVATTN_ERR_HIP = 4
+FVATTN_DENSE = 0
+FVATTN_BLOCK_SPARSE = 1
+TILE = 128
+HEAD_DIM = 128
+MAX_TILES = 2048
+
+_MODES = {"dense": FVATTN_DENSE, "sparse": FVATTN_BLOCK_SPARSE,
+          FVATTN_DENSE: FVATTN_DENSE, FVATTN_BLOCK_SPARSE: FVATTN_BLOCK_SPARSE}
+
+_lib = None
+
+# (name, restype, argtypes) of every exported function
+_P, _I, _F, _D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+SIGNATURES = {
+    "fvattn_keep_count": (_I, [_I, _D]),
+    "fvattn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _D, _P]),
+    "fvattn_select_tiles": (_I, [_P, _P, _I, _I, _I, _D, _P, _P]),
+    "fvattn_forward_indexed": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _F, _P]),
+    "fvattn_forward_heads": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _D, _P]),
+    "fvattn_tile_means": (_I, [_P, _I, _I, _I, _P, _P]),
+    "fvattn_tile_scores": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "fvattn_status_string": (ctypes.c_char_p, [_I]),
+}
+
+
+class FvattnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(status_string(status))
+
+
+def load(path: str = LIB_PATH):
+    """Load libfvattn.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libfvattn.so is not built (%s); run `python -m video_diffusion_transformer_amd.build`"
+            % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fvattn_status_string(int(status)).decode()
+
+
+def _check(rc: int):
+    if rc != FVATTN_OK:
+        raise FvattnError(rc)
+
+
+def keep_count(tokens: int, keep_frac: float) -> int:
+    k = load().fvattn_keep_count(int(tokens), float(keep_frac))
+    if k < 0:
+        raise FvattnError(-k)
+    return k
+
+
+def tile_count(tokens: int) -> int:
+    return -(-int(tokens) // TILE)
+
+
+# ---------------------------------------------------------------- torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_qkv(*ts, shape=None):
+    torch = _torch()
+    ref = ts[0]
+    if ref.dim() != 3:
+        raise ValueError("expected [heads, tokens, head_dim] tensors")
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("expected bfloat16 tensors")
+        if not t.is_cuda:
+            raise ValueError("expected device tensors")
+        if not t.is_contiguous():
+            raise ValueError("expected contiguous tensors")
+        if t.shape != ref.shape or t.device != ref.device:
+            raise ValueError("q, k, v (and out) must share shape and device")
+    return ref.shape
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def forward(q, k, v, scale: float | None = None, mode="dense", keep_frac: float = 0.1,
+            out=None, stream=None):
+    """fvattn_forward.  q, k, v: bf16 [heads, tokens, 128] device tensors."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, N, d, scale,
+                                     _MODES[mode], float(keep_frac), _stream_ptr(stream)))
+    return out
+
+
+def forward_heads(q, k, v, group_heads: int, scale: float | None = None, mode="dense",
+                  keep_frac: float = 0.1, out=None, stream=None):
+    """fvattn_forward_heads: the same attention, launched in head groups of 16, 8 or 4."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_forward_heads(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, int(group_heads),
+                                           N, d, scale, _MODES[mode], float(keep_frac),
+                                           _stream_ptr(stream)))
+    return out
+
+
+def select_tiles(q, k, keep_frac: float = 0.1, out=None, stream=None):
+    """fvattn_select_tiles: int32 [heads, T, keep] kept key tiles per query tile."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k)
+    kk = keep_count(N, keep_frac)
+    if out is None:
+        out = torch.empty((H, tile_count(N), kk), dtype=torch.int32, device=q.device)
+    if out.dtype != torch.int32 or not out.is_contiguous() or tuple(out.shape) != (H, tile_count(N), kk):
+        raise ValueError("idx out must be contiguous int32 [heads, T, keep]")
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_select_tiles(_ptr(q), _ptr(k), H, N, d, float(keep_frac), _ptr(out),
+                                          _stream_ptr(stream)))
+    return out
+
+
+def forward_indexed(q, k, v, idx, scale: float | None = None, out=None, stream=None):
+    """fvattn_forward_indexed: sparse attention over caller-given tile lists idx [heads, T, keep]."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 3 \
+            or idx.shape[0] != H or idx.shape[1] != tile_count(N) or idx.device != q.device:
+        raise ValueError("idx must be contiguous int32 [heads, T, keep] on the device of q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_forward_indexed(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(idx.shape[2]),
+                                             _ptr(out), H, N, d, scale, _stream_ptr(stream)))
+    return out
+
+
+def tile_means(x, stream=None):
+    """fvattn_tile_means: fp64 [heads, T, 128] tile means of a bf16 [heads, tokens, 128] tensor."""
+    torch = _torch()
+    H, N, d = _check_qkv(x)
+    out = torch.empty((H, tile_count(N), d), dtype=torch.float64, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(load().fvattn_tile_means(_ptr(x), H, N, d, _ptr(out), _stream_ptr(stream)))
+    return out
+
+
+def tile_scores(qm, km, stream=None):
+    """fvattn_tile_scores: fp64 [heads, T, T] canonical scores of fp64 tile means."""
+    torch = _torch()
+    if qm.dtype != torch.float64 or km.dtype != torch.float64 or qm.shape != km.shape \
+            or qm.dim() != 3 or not qm.is_contiguous() or not km.is_contiguous():
+        raise ValueError("expected contiguous float64 [heads, T, 128] means")
+    H, T, d = qm.shape
+    out = torch.empty((H, T, T), dtype=torch.float64, device=qm.device)
+    with torch.cuda.device(qm.device):
+        _check(load().fvattn_tile_scores(_ptr(qm), _ptr(km), H, T, d, _ptr(out), _stream_ptr(stream)))
+    return out

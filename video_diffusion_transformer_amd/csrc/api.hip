@@ -1,0 +1,281 @@
+// C ABI of the video-token attention library (declared in include/fvattn.h).
+//
+// Host side only: argument checks (all of them before any HIP call), the
+// keep count of compute_topk, stream-ordered scratch for the sparse mode, and
+// the head-group loop.  Every step of the computation runs in the kernels of
+// attn_fwd.hip and select.hip.
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/fvattn.h"
+#include "fvattn_internal.h"
+
+namespace {
+
+using fvattn::kHeadDim;
+using fvattn::kTile;
+
+constexpr long long kMaxPerHead = (1LL << 31) - 1;   // elements of one head's tensor
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];        // 0 unknown, 1 gfx950, 2 other
+
+int tiles_of(int tokens) { return tokens == 0 ? 0 : (tokens - 1) / kTile + 1; }
+
+bool keep_frac_ok(double f) { return f > 0.0 && f <= 1.0; }   // false for NaN
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+int keep_of(int tiles, double keep_frac) {
+  if (tiles == 0) return 0;
+  const double want = ceil(keep_frac * (double)tiles);
+  if (want >= (double)tiles) return tiles;
+  return want < 1.0 ? 1 : (int)want;
+}
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FVATTN_ERR_UNSUPPORTED;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FVATTN_ERR_HIP;
+    st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (st == 1) {
+      // keep freed stream-ordered scratch in the pool between calls
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t threshold = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+      }
+    }
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FVATTN_OK : FVATTN_ERR_UNSUPPORTED;
+}
+
+bool test_fail_alloc() {
+  const char* e = getenv("FVATTN_TEST_FAIL_ALLOC");
+  return e && e[0] == '1';
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FVATTN_OK : FVATTN_ERR_HIP; }
+
+// Scratch of one sparse call: tile means of Q [H][T][128], transposed tile
+// means of K [H][128][T], and the kept tile lists [H][T][keep].
+struct SparseScratch {
+  void* base = nullptr;
+  double* qm = nullptr;
+  double* kmT = nullptr;
+  int32_t* idx = nullptr;
+};
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_idx,
+                  hipStream_t stream) {
+  const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
+  const size_t idxb = need_idx ? align256(sizeof(int32_t) * (size_t)heads * tiles * keep) : 0;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  if (hipMallocAsync(&s->base, 2 * means + idxb, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    s->base = nullptr;
+    return FVATTN_ERR_ALLOC;
+  }
+  char* p = (char*)s->base;
+  s->qm = (double*)p;
+  s->kmT = (double*)(p + means);
+  s->idx = need_idx ? (int32_t*)(p + 2 * means) : nullptr;
+  return FVATTN_OK;
+}
+
+int scratch_free(SparseScratch* s, hipStream_t stream) {
+  if (!s->base) return FVATTN_OK;
+  return hip_status(hipFreeAsync(s->base, stream));
+}
+
+// Selection into idx (S1-S3) for heads already validated.
+int run_selection(const uint16_t* q, const uint16_t* k, int heads, int tokens, int keep,
+                  const SparseScratch& s, int32_t* idx, hipStream_t stream) {
+  const int T = tiles_of(tokens);
+  hipError_t e = fvattn::launch_tile_means(q, s.qm, heads, tokens, false, stream);
+  if (e == hipSuccess) e = fvattn::launch_tile_means(k, s.kmT, heads, tokens, true, stream);
+  if (e == hipSuccess) e = fvattn::launch_score_select(s.qm, s.kmT, heads, T, keep, idx, nullptr, stream);
+  return hip_status(e);
+}
+
+// Forward for one validated launch of `heads` heads.
+int forward_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int heads,
+                int tokens, float scale, int mode, double keep_frac, hipStream_t stream) {
+  if (mode == FVATTN_DENSE)
+    return hip_status(fvattn::launch_attention(q, k, v, out, nullptr, 0, heads, tokens, scale, stream));
+  const int T = tiles_of(tokens);
+  const int keep = keep_of(T, keep_frac);
+  SparseScratch s;
+  int rc = scratch_alloc(&s, heads, T, keep, true, stream);
+  if (rc != FVATTN_OK) return rc;
+  rc = run_selection(q, k, heads, tokens, keep, s, s.idx, stream);
+  if (rc == FVATTN_OK)
+    rc = hip_status(fvattn::launch_attention(q, k, v, out, s.idx, keep, heads, tokens, scale, stream));
+  const int rf = scratch_free(&s, stream);
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+// Checks shared by the forward entry points, in the documented order.  Returns
+// FVATTN_OK and sets *empty when there is nothing to do.
+int check_forward_args(const void* q, const void* k, const void* v, const void* out, int heads,
+                       int tokens, int head_dim, float scale, int mode, double keep_frac,
+                       bool* empty) {
+  *empty = false;
+  if (mode != FVATTN_DENSE && mode != FVATTN_BLOCK_SPARSE) return FVATTN_ERR_INVALID_ARG;
+  if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FVATTN_ERR_INVALID_ARG;
+  if (mode == FVATTN_BLOCK_SPARSE && !keep_frac_ok(keep_frac)) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) {
+    *empty = true;
+    return FVATTN_OK;
+  }
+  if (!q || !k || !v || !out) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
+  if (mode == FVATTN_BLOCK_SPARSE && tiles_of(tokens) > FVATTN_MAX_TILES)
+    return FVATTN_ERR_UNSUPPORTED;
+  return FVATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fvattn_keep_count(int tokens, double keep_frac) {
+  if (tokens < 0 || !keep_frac_ok(keep_frac)) return -FVATTN_ERR_INVALID_ARG;
+  return keep_of(tiles_of(tokens), keep_frac);
+}
+
+int fvattn_forward(const void* q, const void* k, const void* v, void* out, int heads, int tokens,
+                   int head_dim, float scale, int mode, double keep_frac, void* stream) {
+  bool empty;
+  int rc = check_forward_args(q, k, v, out, heads, tokens, head_dim, scale, mode, keep_frac, &empty);
+  if (rc != FVATTN_OK || empty) return rc;
+  if (mode == FVATTN_BLOCK_SPARSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  return forward_one((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
+                     heads, tokens, scale, mode, keep_frac, (hipStream_t)stream);
+}
+
+int fvattn_select_tiles(const void* q, const void* k, int heads, int tokens, int head_dim,
+                        double keep_frac, int32_t* idx_out, void* stream) {
+  if (heads < 0 || tokens < 0 || !keep_frac_ok(keep_frac)) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) return FVATTN_OK;
+  if (!q || !k || !idx_out) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead || tiles_of(tokens) > FVATTN_MAX_TILES)
+    return FVATTN_ERR_UNSUPPORTED;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = tiles_of(tokens);
+  const int keep = keep_of(T, keep_frac);
+  SparseScratch s;
+  rc = scratch_alloc(&s, heads, T, keep, false, st);
+  if (rc != FVATTN_OK) return rc;
+  rc = run_selection((const uint16_t*)q, (const uint16_t*)k, heads, tokens, keep, s, idx_out, st);
+  const int rf = scratch_free(&s, st);
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_forward_indexed(const void* q, const void* k, const void* v, const int32_t* idx,
+                           int keep, void* out, int heads, int tokens, int head_dim, float scale,
+                           void* stream) {
+  if (heads < 0 || tokens < 0 || !scale_ok(scale)) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) return FVATTN_OK;
+  if (!q || !k || !v || !idx || !out) return FVATTN_ERR_INVALID_ARG;
+  if (keep < 1 || keep > tiles_of(tokens)) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  return hip_status(fvattn::launch_attention((const uint16_t*)q, (const uint16_t*)k,
+                                             (const uint16_t*)v, (uint16_t*)out, idx, keep, heads,
+                                             tokens, scale, (hipStream_t)stream));
+}
+
+int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out, int total_heads,
+                         int group_heads, int tokens, int head_dim, float scale, int mode,
+                         double keep_frac, void* stream) {
+  bool empty;
+  int rc = check_forward_args(q, k, v, out, total_heads, tokens, head_dim, scale, mode, keep_frac,
+                              &empty);
+  if (rc != FVATTN_OK) return rc;
+  if (group_heads != 16 && group_heads != 8 && group_heads != 4) return FVATTN_ERR_UNSUPPORTED;
+  if (empty) return FVATTN_OK;
+  if (mode == FVATTN_BLOCK_SPARSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  const size_t per_head = (size_t)tokens * kHeadDim;
+  for (int h0 = 0; h0 < total_heads; h0 += group_heads) {
+    const int n = (total_heads - h0 < group_heads) ? total_heads - h0 : group_heads;
+    const size_t off = (size_t)h0 * per_head;
+    rc = forward_one((const uint16_t*)q + off, (const uint16_t*)k + off, (const uint16_t*)v + off,
+                     (uint16_t*)out + off, n, tokens, scale, mode, keep_frac, (hipStream_t)stream);
+    if (rc != FVATTN_OK) return rc;
+  }
+  return FVATTN_OK;
+}
+
+int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double* means_out,
+                      void* stream) {
+  if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) return FVATTN_OK;
+  if (!x || !means_out) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  return hip_status(fvattn::launch_tile_means((const uint16_t*)x, means_out, heads, tokens, false,
+                                              (hipStream_t)stream));
+}
+
+int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles, int head_dim,
+                       double* scores_out, void* stream) {
+  if (heads < 0 || tiles < 0) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tiles == 0) return FVATTN_OK;
+  if (!qm || !km || !scores_out) return FVATTN_ERR_INVALID_ARG;
+  if (tiles > FVATTN_MAX_TILES) return FVATTN_ERR_UNSUPPORTED;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  void* kmT = nullptr;
+  if (hipMallocAsync(&kmT, sizeof(double) * (size_t)heads * tiles * kHeadDim, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  hipError_t e = fvattn::launch_transpose_means(km, (double*)kmT, heads, tiles, st);
+  if (e == hipSuccess)
+    e = fvattn::launch_score_select(qm, (const double*)kmT, heads, tiles, 0, nullptr, scores_out, st);
+  rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(kmT, st));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+const char* fvattn_status_string(int status) {
+  switch (status) {
+    case FVATTN_OK: return "FVATTN_OK: success";
+    case FVATTN_ERR_INVALID_ARG: return "FVATTN_ERR_INVALID_ARG: invalid argument";
+    case FVATTN_ERR_UNSUPPORTED: return "FVATTN_ERR_UNSUPPORTED: unsupported shape, size or device";
+    case FVATTN_ERR_ALLOC: return "FVATTN_ERR_ALLOC: scratch allocation failed";
+    case FVATTN_ERR_HIP: return "FVATTN_ERR_HIP: HIP runtime or launch error";
+    default: return "FVATTN: unknown status";
+  }
+}
+
+}  // extern "C"

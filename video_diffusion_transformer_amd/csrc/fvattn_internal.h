@@ -1,0 +1,36 @@
+// Internal launch interface between the C ABI (api.hip) and the gfx950 kernels.
+// Not installed; every pointer here has already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fvattn {
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 128;        // selection tile (tokens)
+
+// Dense (idx == nullptr) or tile-list (idx != nullptr, `keep` entries per query
+// tile) attention forward over `heads` heads.
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            uint16_t* out, const int32_t* idx, int keep, int heads, int tokens,
+                            float scale, hipStream_t stream);
+
+// S1: fp64 tile means.  transposed == false: out [heads][T][128];
+// transposed == true: out [heads][128][T].
+hipError_t launch_tile_means(const uint16_t* x, double* out, int heads, int tokens,
+                             bool transposed, hipStream_t stream);
+
+// S2 + S3: canonical fp64 scores of qm [heads][T][128] against kmT
+// [heads][128][T]; with scores_out != nullptr the scores are written
+// [heads][T][T] and no selection happens, otherwise the top `keep` tiles of
+// every row go to idx_out [heads][T][keep], ascending.
+hipError_t launch_score_select(const double* qm, const double* kmT, int heads, int tiles,
+                               int keep, int32_t* idx_out, double* scores_out,
+                               hipStream_t stream);
+
+// [heads][T][128] -> [heads][128][T] (fp64), for the score diagnostic entry.
+hipError_t launch_transpose_means(const double* in, double* out, int heads, int tiles,
+                                  hipStream_t stream);
+
+}  // namespace fvattn
