@@ -1,0 +1,256 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+Workload: 72,576 video tokens (a 10 s 1344x768 clip, 72 latent frames of 1,008
+tokens) x 56 heads of width 128, bf16, frame-correlated synthetic Q/K and
+N(0, 1) V, seed 3.  One step is one pass of the whole path over that input:
+the dense attention of all 56 heads through the head-group launcher (groups of
+16: 16+16+16+8), then the 90%-sparse attention of all 56 heads through the same
+launcher (per group: tile means, tile scores and top-57 selection, sparse tile
+loop).  Inputs are resident in HBM before timing starts.
+
+Effective FLOP (the count used for every TFLOP/s figure): 4 * d * (valid keys
+attended) summed over heads and valid query rows; dense = 4 N^2 d H, sparse is
+counted exactly from the selected tile lists (a partial tile counts its valid
+keys).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_dense_72576x56_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", "attn_fwd.hip")
+
+TOKENS, HEADS, GROUP, KEEP_FRAC, SEED = 72576, 56, 16, 0.1, 3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def sparse_flops(idx, tokens: int, d: int = 128) -> float:
+    """4 d (valid keys) summed over heads and valid query rows, from int32 idx [H, T, k]."""
+    import numpy as np
+    T = idx.shape[1]
+    valid = np.full(T, 128, dtype=np.int64)
+    valid[-1] = tokens - 128 * (T - 1)
+    keys = valid[idx].sum(axis=2)            # [H, T] keys seen by each query tile
+    return float(4 * d * (keys * valid[None, :]).sum())
+
+
+def cpu_baseline(q, k, v, scale, budget_s: float):
+    """The fp64 oracle on head 0 of the same workload: full selection, then dense and
+    sparse attention for consecutive query tiles until the time budget is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qw, kw, vw = (oracle.widen(t[:1]) for t in (q, k, v))
+    t0 = time.perf_counter()
+    idx = oracle.select_tiles(qw, kw, KEEP_FRAC)
+    t_sel = time.perf_counter() - t0
+    T = idx.shape[1]
+    flop = 0.0
+    tiles = 0
+    elapsed = t_sel
+    while tiles < T and elapsed < budget_s:
+        rows = np.arange(tiles * 128, min(tiles * 128 + 128, TOKENS))
+        t1 = time.perf_counter()
+        oracle.dense(qw, kw, vw, scale, rows=rows)
+        oracle.sparse(qw, kw, vw, scale, idx, rows=rows)
+        elapsed += time.perf_counter() - t1
+        keys = sum(min(128, TOKENS - 128 * t) for t in idx[0, tiles])
+        flop += 4 * 128 * len(rows) * (TOKENS + keys)
+        tiles += 1
+    # the selection of one head is 1/56 of the workload's selection; charge it fully
+    value = flop / elapsed / 1e12
+    return {
+        "value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, head 0 of {HEADS}: tile selection over all {T} tiles "
+                   f"({t_sel:.1f} s), then dense and 90%-sparse attention for query tiles 0-{tiles - 1} "
+                   f"({tiles * 128} rows), {elapsed:.1f} s in total; effective FLOP of those rows / time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["dense", "sparse"], default=None,
+                    help="time only one of the two modes (for profiler runs; value then covers that mode)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for HBM counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU launch; heads would shard with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import video_diffusion_transformer_amd as fv
+    from video_diffusion_transformer_amd import inputs
+
+    fv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scale = 1.0 / math.sqrt(128)
+
+    log("generating inputs", TOKENS, "tokens x", HEADS, "heads")
+    q, k, v = inputs.make_qkv(TOKENS, HEADS, "frame", SEED)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out_dense = torch.empty_like(qd)
+    out_sparse = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    idx = fv.select_tiles(qd, kd, keep_frac=KEEP_FRAC)
+    torch.cuda.synchronize()
+    flop_sparse = sparse_flops(idx.cpu().numpy(), TOKENS)
+    flop_dense = 4.0 * TOKENS * TOKENS * 128 * HEADS
+    n_launch = math.ceil(HEADS / GROUP)
+    del idx
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+        del a, b
+
+    do_dense = args.only in (None, "dense")
+    do_sparse = args.only in (None, "sparse")
+    if not do_dense:
+        flop_dense = 0.0
+    if not do_sparse:
+        flop_sparse = 0.0
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if do_dense:
+            fv.forward_heads(qd, kd, vd, GROUP, scale=scale, mode="dense", out=out_dense)
+        if ev is not None:
+            ev[1].record(stream)
+        if do_sparse:
+            fv.forward_heads(qd, kd, vd, GROUP, scale=scale, mode="sparse", keep_frac=KEEP_FRAC,
+                             out=out_sparse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dense_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sparse_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / args.steps
+
+    # split of the sparse time: selection alone, outside the timed region
+    sel_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    idx_buf = torch.empty((GROUP, fv.tile_count(TOKENS), fv.keep_count(TOKENS, KEEP_FRAC)),
+                          dtype=torch.int32, device=dev)
+    sel_ms = []
+    for _ in range(3):
+        sel_ev[0].record(stream)
+        for h0 in range(0, HEADS, GROUP):
+            h1 = min(HEADS, h0 + GROUP)
+            fv.select_tiles(qd[h0:h1], kd[h0:h1], keep_frac=KEEP_FRAC, out=idx_buf[:h1 - h0])
+        sel_ev[1].record(stream)
+        torch.cuda.synchronize()
+        sel_ms.append(sel_ev[0].elapsed_time(sel_ev[1]))
+
+    d_ms = float(np.median(dense_ms))
+    s_ms = float(np.median(sparse_ms))
+    dense_tflops = flop_dense / max(d_ms * 1e-3, 1e-12) / 1e12
+    sparse_tflops = flop_sparse / max(s_ms * 1e-3, 1e-12) / 1e12
+    value = (flop_dense + flop_sparse) * args.steps / wall / 1e12
+
+    # roofline of the dominant kernel (the dense attention launches): per launch
+    # = the average head-group launch (56 heads in 4 launches)
+    dense_launch_ms = d_ms / n_launch
+    achieved = (flop_dense / n_launch) / max(dense_launch_ms * 1e-3, 1e-12) / 1e12
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attn_fwd_kernel<false> (dense)",
+                "avg_launch_ms": round(dense_launch_ms, 4)}
+
+    result = {
+        "metric": "attn TFLOP/s + % bf16 MFMA peak, 72,576 tok x 56 heads, dense & 90% sparse",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded frame-correlated Q/K, N(0,1) V; stands in for H3 activations)",
+        "config": {"workload": "video-token attention, 72,576 tokens x 56 heads x 128, "
+                               "dense + 90% block-sparse (57 of 567 key tiles), head groups of 16",
+                   "tokens": TOKENS, "heads": HEADS, "head_dim": 128, "group_heads": GROUP,
+                   "keep_frac": KEEP_FRAC, "seed": SEED},
+        "dense": {"ms": round(d_ms, 3), "tflops": round(dense_tflops, 2),
+                  "frac_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4), "flop": flop_dense},
+        "sparse": {"ms": round(s_ms, 3), "tflops_effective": round(sparse_tflops, 2),
+                   "frac_peak": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "flop": flop_sparse,
+                   "selection_ms": round(float(np.median(sel_ms)), 3),
+                   "speedup_vs_dense": round(d_ms / s_ms, 3) if do_dense and do_sparse else None},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), budget", args.cpu_budget, "s")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -233,6 +233,7 @@ def cfg5():
     return inputs.make_inputs(5)
 
 
+@pytest.mark.timeout(300)
 def test_config3_dense_sampled():
     c = inputs.CONFIGS[3]
     say("config", c.name)
@@ -269,9 +270,11 @@ def _full_size_sparse_and_dense(cid, qkv):
         del out
 
 
+@pytest.mark.timeout(400)
 def test_config4_sparse_and_dense(cfg4):
     _full_size_sparse_and_dense(4, cfg4)
 
 
+@pytest.mark.timeout(400)
 def test_config5_sparse_and_dense(cfg5):
     _full_size_sparse_and_dense(5, cfg5)

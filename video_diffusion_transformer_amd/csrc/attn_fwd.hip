@@ -79,6 +79,7 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+template <bool kSparse>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, const int32_t* __restrict__ idx,
@@ -105,10 +106,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     qf[dk] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const int32_t* irow = idx ? idx + ((size_t)h * qtiles + qt) * keep : nullptr;
-  const int nsub = idx ? 2 * keep : (N + kBN - 1) / kBN;
+  const int32_t* irow = kSparse ? idx + ((size_t)h * qtiles + qt) * keep : nullptr;
+  const int nsub = kSparse ? 2 * keep : (N + kBN - 1) / kBN;
   auto kv_start = [&](int it) -> int {
-    if (!irow) return it * kBN;
+    if (!kSparse) return it * kBN;
     int t = irow[it >> 1];
     t = t < 0 ? 0 : (t >= qtiles ? qtiles - 1 : t);
     return t * kTile + (it & 1) * kBN;
@@ -279,8 +280,12 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   const long long blocks = (long long)heads * qtiles;
   if (blocks <= 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, k, v,
-                     out, idx, keep, tokens, qtiles, c);
+  if (idx)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
+                       k, v, out, idx, keep, tokens, qtiles, c);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
+                       k, v, out, idx, keep, tokens, qtiles, c);
   return hipGetLastError();
 }
 
