@@ -14,21 +14,30 @@
 //   the whole kernel) and O^T = V^T P^T (A = V^T from LDS, B = P^T taken
 //   straight from the S^T accumulators).  With this orientation every lane owns
 //   one query column of S^T and of O^T, so the softmax max/sum and the O
-//   rescale are per-lane scalars plus one exchange between the two half-waves.
+//   rescale are per-lane scalars plus one swap between the two half-waves
+//   (v_permlane32_swap, no LDS traffic).
 // * The key rows fed to the S^T product are permuted inside each 32-key block
 //   so that half-wave g ends up holding keys 16g..16g+15 contiguously; P^T can
 //   then be passed to the PV product without any data movement.
 // * K and V stream through LDS in 64-key stages, double buffered: the next
-//   stage's 128-bit global loads are in flight while the current stage is
-//   multiplied.  K is stored row-major with an XOR swizzle on 16-byte chunks;
-//   V is transposed on the way in (key-contiguous rows per head dimension),
-//   also swizzled, so that every MFMA operand is one 128-bit LDS read.
+//   stage's 128-bit buffer loads are in flight while the current stage is
+//   multiplied.  The buffer descriptor of each stage starts at the stage's first
+//   key and ends at the last token, so the hardware range check zero-fills the
+//   rows past the sequence end with no branches.  K and V are both stored
+//   row-major with XOR swizzles on 16-byte chunks.  The V^T operand is read with
+//   the gfx950 LDS transpose load (ds_read_b64_tr_b16), two per MFMA.
 // * fp32 online softmax in the exp2 domain (scale * log2 e folded into one
-//   FMA per score), P rounded to bf16 for the PV product, out rounded to bf16.
+//   FMA per score).  The running max is only raised, and O and the running sum
+//   rescaled, when some row of the wave sees a score more than 2^8 above it
+//   (wave-uniform branch); otherwise P may reach 2^8, which fp32 and bf16 hold
+//   exactly as well as they hold 1.  P is rounded to bf16 for the PV product,
+//   out to bf16.
 // * Workgroups are remapped so each of the 8 XCDs walks a contiguous range of
 //   (head, query tile) pairs, keeping one head's K/V hot in that XCD's L2.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "fvattn_internal.h"
 
@@ -39,6 +48,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kBM = 128;                    // query rows per workgroup
 constexpr int kBN = 64;                     // keys per LDS stage
@@ -49,14 +60,17 @@ constexpr int kVStage = kBN * kRowBytes;    // 16 KiB
 constexpr int kStage = kKStage + kVStage;
 constexpr int kLds = 2 * kStage;            // 64 KiB, two workgroups per CU
 constexpr int kXcds = 8;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
 
-// K rows: chunk (16 B) swizzle; rows read together by one MFMA phase map to
-// distinct chunk positions.
+// K rows: chunk (16 B) swizzle; the 16 rows read by lanes 0..15 (and by 16..31)
+// of one S^T operand load land on 16 distinct chunk positions.
 __device__ __forceinline__ int k_swz(int row) {
   return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
 }
-// V^T rows (one per head dimension, 64 keys = 8 chunks).
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// V rows: the 4 consecutive keys read by one 16-lane group of a transpose load
+// land on distinct chunk positions.
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
 // Key (within a 32-key block) fed as A-row m of the S^T product: output row m
 // lands in half-wave (m>>2)&1 at accumulator 4*(m>>3) + (m&3), so this puts
@@ -72,11 +86,19 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes,
+                                           kBufferFlags);
 }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+
+// Combine x with its value in the other half-wave (lane l and lane l ^ 32).
+__device__ __forceinline__ float halfwave_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <bool kSparse>
@@ -88,22 +110,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int h = L / qtiles, qt = L - h * qtiles;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const size_t hoff = (size_t)h * (size_t)N * kHeadDim;
-  const uint16_t* Qh = Q + hoff;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
 
   // Q^T fragment of this lane's query row (B operand of S^T = K Q^T):
-  // qf[dk][i] = Q[qrow][16 dk + 8 g + i].
-  const int qrow = qt * kBM + wave * 32 + l32;
+  // qf[dk][i] = Q[qrow][16 dk + 8 g + i]; rows past N read as zero.
+  const int q0 = qt * kBM + wave * 32;
+  const int qrow = q0 + l32;
   bf16x8 qf[8];
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
 #pragma unroll
-  for (int dk = 0; dk < 8; ++dk) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < N) w = *(const u32x4*)(Qh + (size_t)qrow * kHeadDim + 16 * dk + 8 * g);
-    qf[dk] = __builtin_bit_cast(bf16x8, w);
+    for (int dk = 0; dk < 8; ++dk) {
+      const u32x4 w =
+          __builtin_amdgcn_raw_buffer_load_b128(rq, l32 * kRowBytes + 32 * dk + 16 * g, 0, 0);
+      qf[dk] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   const int32_t* irow = kSparse ? idx + ((size_t)h * qtiles + qt) * keep : nullptr;
@@ -115,45 +142,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     return t * kTile + (it & 1) * kBN;
   };
 
-  // Global -> register staging: K rows (tid>>4) + 16 rr, V rows 4 (tid>>4) + rr,
-  // 16-byte chunk tid & 15 of each row; rows past N read as zero.
+  // Global -> register staging: K and V rows rg + 16 rr, 16-byte chunk ch.
   const int ch = tid & 15, rg = tid >> 4;
   u32x4 kr[4], vr[4];
   auto load_kv = [&](int kv0) {
+    const int rem = (N - kv0) * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * kHeadDim, rem);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * kHeadDim, rem);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int kk = kv0 + rg + 16 * rr;
-      const int vk = kv0 + 4 * rg + rr;
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (kk < N) a = *(const u32x4*)(Kh + (size_t)kk * kHeadDim + 8 * ch);
-      if (vk < N) b = *(const u32x4*)(Vh + (size_t)vk * kHeadDim + 8 * ch);
-      kr[rr] = a;
-      vr[rr] = b;
+      const int off = (rg + 16 * rr) * kRowBytes + 16 * ch;
+      kr[rr] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      vr[rr] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   };
-  auto store_kv = [&](int buf) {
-    unsigned char* Ks = smem + buf * kStage;
-    unsigned char* Vt = Ks + kKStage;
+  auto store_kv = [&](auto bufc) {
+    unsigned char* Ks = smem + decltype(bufc)::value * kStage;
+    unsigned char* Vs = Ks + kKStage;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int row = rg + 16 * rr;
       *(u32x4*)(Ks + row * kRowBytes + ((ch ^ k_swz(row)) << 4)) = kr[rr];
-    }
-    // transpose 4 keys x 8 dims into 8 rows of V^T (4 keys = 8 bytes each)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * ch + e;
-      const int w = e >> 1;
-      u32x2 val;
-      if ((e & 1) == 0) {
-        val[0] = pack_lo(vr[0][w], vr[1][w]);
-        val[1] = pack_lo(vr[2][w], vr[3][w]);
-      } else {
-        val[0] = pack_hi(vr[0][w], vr[1][w]);
-        val[1] = pack_hi(vr[2][w], vr[3][w]);
-      }
-      const int chunk = rg >> 1, half = rg & 1;
-      *(u32x2*)(Vt + d * 128 + ((chunk ^ v_swz(d)) << 4) + half * 8) = val;
+      *(u32x4*)(Vs + row * kRowBytes + ((ch ^ v_swz(row)) << 4)) = vr[rr];
     }
   };
 
@@ -164,20 +174,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int krow = key_of_row(l32);
-  const int ksw = k_swz(krow);
+  // S^T operand: row key_of_row(l32) (+32 for the second 32-key block), chunk
+  // 2 dk + g; byte offsets within a stage, one per dk (the +32 rows and the
+  // stage are immediate offsets).
+  int koff[8];
+  {
+    const int krow = key_of_row(l32);
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk) koff[dk] = krow * kRowBytes + (((2 * dk + g) ^ k_swz(krow)) << 4);
+  }
+  // V^T operand by transpose load: 16-lane group G = lane >> 4 covers head
+  // dims 32 db + 16 (G & 1) + 0..15 and keys 32 kb + 16 (G >> 1) + 8 s + 0..7;
+  // source lane s16 = lane & 15 reads 4 dims of key (s16 >> 2) (then + 4).
+  // Byte offsets within a stage, one per db; the key steps (32 kb + 8 s, and
+  // +4 for the second read) are whole rows and keep (key & 3), so they are
+  // immediate offsets.
+  int voff[4];
+  {
+    const int s16 = lane & 15, G = lane >> 4;
+    const int vkey = 16 * (G >> 1) + (s16 >> 2);
+    const int vdim = 16 * (G & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int dim = vdim + 32 * db;
+      voff[db] = kKStage + vkey * kRowBytes + (((dim >> 3) ^ v_swz(vkey)) << 4) + 8 * ((dim >> 2) & 1);
+    }
+  }
 
-  auto compute = [&](int buf, int kv0) {
-    const unsigned char* Ks = smem + buf * kStage;
-    const unsigned char* Vt = Ks + kKStage;
+  auto compute = [&](auto bufc, int kv0) {
+    const unsigned char* st_base = smem + decltype(bufc)::value * kStage;
     f32x16 s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
     for (int dk = 0; dk < 8; ++dk) {
-      const int cpos = ((2 * dk + g) ^ ksw) << 4;
-      const bf16x8 a0 = *(const bf16x8*)(Ks + krow * kRowBytes + cpos);
-      const bf16x8 a1 = *(const bf16x8*)(Ks + (krow + 32) * kRowBytes + cpos);
+      const bf16x8 a0 = *(const bf16x8*)(st_base + koff[dk]);
+      const bf16x8 a1 = *(const bf16x8*)(st_base + koff[dk] + 32 * kRowBytes);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[dk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[dk], s1, 0, 0, 0);
     }
@@ -194,23 +226,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mx = halfwave_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_use));
-      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_use));
+      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_run));
+      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_run));
       psum += s0[r] + s1[r];
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    l_run += psum;
 
     bf16x8 p[4];
 #pragma unroll
@@ -220,47 +254,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       p[2][i] = (__bf16)s1[i];
       p[3][i] = (__bf16)s1[8 + i];
     }
-    // O^T += V^T P^T; step (kb, s) covers keys 32 kb + 16 g + 8 s + 0..7
+    // O^T += V^T P^T; step st = 2 kb + s covers keys 32 kb + 16 g + 8 s + 0..7
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + l32;
-      const unsigned char* vrow = Vt + d * 128;
-      const int sw = v_swz(d);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int chunk = 4 * (st >> 1) + 2 * g + (st & 1);
-        const bf16x8 a = *(const bf16x8*)(vrow + ((chunk ^ sw) << 4));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[st], oacc[db], 0, 0, 0);
+        const unsigned char* r0 = st_base + voff[db] + (32 * (st >> 1) + 8 * (st & 1)) * kRowBytes;
+        const unsigned char* r1 = r0 + 4 * kRowBytes;
+        const u32x2 lo =
+            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r0));
+        const u32x2 hi =
+            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r1));
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), p[st],
+                                                           oacc[db], 0, 0, 0);
       }
     }
   };
 
-  load_kv(kv_start(0));
-  store_kv(0);
-  __syncthreads();
-  for (int it = 0; it < nsub; ++it) {
-    const int buf = it & 1;
+  // One stage: prefetch stage it+1 into registers, multiply stage it out of
+  // LDS buffer `buf`, then park stage it+1 in the other buffer.  The loop is
+  // unrolled by two so the buffer (and every LDS address offset) is a constant.
+  auto step = [&](auto bufc, int it) {
+    constexpr int buf = decltype(bufc)::value;
     const int kv0 = kv_start(it);
     const bool more = it + 1 < nsub;
     if (more) load_kv(kv_start(it + 1));
-    if (kv0 < N) compute(buf, kv0);
-    if (more) store_kv(buf ^ 1);
+    if (kv0 < N) compute(bufc, kv0);
+    if (more) store_kv(std::integral_constant<int, buf ^ 1>());
     __syncthreads();
+  };
+  load_kv(kv_start(0));
+  store_kv(std::integral_constant<int, 0>());
+  __syncthreads();
+  for (int it = 0; it < nsub; it += 2) {
+    step(std::integral_constant<int, 0>(), it);
+    if (it + 1 < nsub) step(std::integral_constant<int, 1>(), it + 1);
   }
 
   // O^T accumulators: oacc[db][4 j + i] = O[q][32 db + 8 j + 4 g + i]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / halfwave_sum(l_run);
   if (qrow < N) {
     uint16_t* orow = O + hoff + (size_t)qrow * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __bf16 b0 = (__bf16)(oacc[db][4 * j + 0] * inv);
-        __bf16 b1 = (__bf16)(oacc[db][4 * j + 1] * inv);
-        __bf16 b2 = (__bf16)(oacc[db][4 * j + 2] * inv);
-        __bf16 b3 = (__bf16)(oacc[db][4 * j + 3] * inv);
+        const __bf16 b0 = (__bf16)(oacc[db][4 * j + 0] * inv);
+        const __bf16 b1 = (__bf16)(oacc[db][4 * j + 1] * inv);
+        const __bf16 b2 = (__bf16)(oacc[db][4 * j + 2] * inv);
+        const __bf16 b3 = (__bf16)(oacc[db][4 * j + 3] * inv);
         u32x2 w;
         w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
                ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
