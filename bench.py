@@ -138,11 +138,14 @@ def main():
     del idx
 
     if args.copy_calibration:
-        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB (a device-to-device
+        # copy_ may run on a DMA engine, which the shader counters do not see)
+        a = torch.zeros(1 << 29, dtype=torch.int16, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
         torch.cuda.synchronize()
-        log("copy calibration: 1 GiB read + 1 GiB written")
+        torch.bitwise_not(a, out=b)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written by one elementwise kernel")
         del a, b
 
     do_dense = args.only in (None, "dense")
