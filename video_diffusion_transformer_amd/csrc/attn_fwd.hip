@@ -8,24 +8,35 @@
 // arithmetic"; FastH3 page, section "Lever two: VSA-H3 makes each of the four
 // calls cheaper", fine stage: exact attention over the surviving tiles).
 //
-// Design (one workgroup = one head x one 128-row query tile, 4 waves of 32 rows):
+// Design (one workgroup = one head x one 128-row query tile; 2 waves of 64
+// query rows; 2 workgroups per CU, so one wave per SIMD with the whole
+// 512-entry register file):
 // * Both products run on the bf16 matrix cores, v_mfma_f32_32x32x16_bf16, in
 //   transposed form: S^T = K Q^T (A = K from LDS, B = Q^T held in registers for
 //   the whole kernel) and O^T = V^T P^T (A = V^T from LDS, B = P^T taken
 //   straight from the S^T accumulators).  With this orientation every lane owns
 //   one query column of S^T and of O^T, so the softmax max/sum and the O
 //   rescale are per-lane scalars plus one swap between the two half-waves
-//   (v_permlane32_swap, no LDS traffic).
+//   (v_permlane32_swap, no LDS traffic).  Each wave covers two 32-row query
+//   blocks, so every K or V operand read from LDS feeds two MFMAs.
 // * The key rows fed to the S^T product are permuted inside each 32-key block
 //   so that half-wave g ends up holding keys 16g..16g+15 contiguously; P^T can
 //   then be passed to the PV product without any data movement.
-// * K and V stream through LDS in 64-key stages, double buffered: the next
-//   stage's 128-bit buffer loads are in flight while the current stage is
-//   multiplied.  The buffer descriptor of each stage starts at the stage's first
-//   key and ends at the last token, so the hardware range check zero-fills the
-//   rows past the sequence end with no branches.  K and V are both stored
-//   row-major with XOR swizzles on 16-byte chunks.  The V^T operand is read with
-//   the gfx950 LDS transpose load (ds_read_b64_tr_b16), two per MFMA.
+// * K and V stream through LDS in 32-key stages, double buffered, written by
+//   the buffer-load-to-LDS path (no registers involved).  The buffer
+//   descriptor of each stage starts at the stage's first key and ends at the
+//   last token, so the hardware range check zero-fills rows past the sequence
+//   end.  K and V are stored row-major with XOR swizzles on 16-byte chunks (each
+//   lane fetches the global chunk that belongs at its LDS slot).  The V^T
+//   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
+// * Software pipeline per 32-key stage j: the S^T MFMAs of stage j+1 run while
+//   the softmax of stage j (exp2, row sums, bf16 packing) runs on the vector
+//   ALU; then the PV MFMAs of stage j run while the row max of stage j+1 is
+//   taken.  The interleaving is pinned with scheduling group barriers.  The
+//   scores alternate between two register sets across the two unrolled stages,
+//   so the softmax of one stage and the S^T product of the next never touch
+//   the same registers.  One barrier per stage; the loads of K(j+2) and V(j+1)
+//   are in flight for the whole stage.
 // * fp32 online softmax in the exp2 domain (scale * log2 e folded into one
 //   FMA per score).  The running max is only raised, and O and the running sum
 //   rescaled, when some row of the wave sees a score more than 2^8 above it
@@ -50,18 +61,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 128;                    // query rows per workgroup
 constexpr int kBN = 64;                     // keys per LDS stage
-constexpr int kThreads = 256;               // 4 waves x 32 query rows
+constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
+constexpr int kQB = 1;                      // 32-row query blocks per wave
+constexpr int kWaves = kBM / (32 * kQB);    // 4 waves of 32 query rows
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = kHeadDim * 2;     // 256 B per token row
-constexpr int kKStage = kBN * kRowBytes;    // 16 KiB
-constexpr int kVStage = kBN * kRowBytes;    // 16 KiB
-constexpr int kStage = kKStage + kVStage;
-constexpr int kLds = 2 * kStage;            // 64 KiB, two workgroups per CU
+constexpr int kTileBytes = kBN * kRowBytes; // 16 KiB: one K or V stage
+constexpr int kLds = 4 * kTileBytes;        // K[2], V[2]: 64 KiB, two workgroups per CU
+constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
 constexpr int kXcds = 8;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
+constexpr int kWaitVmcnt0 = 0x0F70;         // s_waitcnt vmcnt(0), other counters untouched
 
 // K rows: chunk (16 B) swizzle; the 16 rows read by lanes 0..15 (and by 16..31)
 // of one S^T operand load land on 16 distinct chunk positions.
@@ -101,6 +116,9 @@ __device__ __forceinline__ float halfwave_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
 template <bool kSparse>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -117,66 +135,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
 
-  // Q^T fragment of this lane's query row (B operand of S^T = K Q^T):
-  // qf[dk][i] = Q[qrow][16 dk + 8 g + i]; rows past N read as zero.
-  const int q0 = qt * kBM + wave * 32;
-  const int qrow = q0 + l32;
-  bf16x8 qf[8];
+  // Q^T fragments of this lane's two query rows (B operands of S^T = K Q^T):
+  // qf[qb][dk][i] = Q[q0 + 32 qb + l32][16 dk + 8 g + i]; rows past N read as 0.
+  const int q0 = qt * kBM + wave * 32 * kQB;
+  bf16x8 qf[kQB][8];
   {
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) {
-      const u32x4 w =
-          __builtin_amdgcn_raw_buffer_load_b128(rq, l32 * kRowBytes + 32 * dk + 16 * g, 0, 0);
-      qf[dk] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int dk = 0; dk < 8; ++dk) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, (32 * qb + l32) * kRowBytes + 32 * dk + 16 * g, 0, 0);
+        qf[qb][dk] = __builtin_bit_cast(bf16x8, w);
+      }
   }
 
   const int32_t* irow = kSparse ? idx + ((size_t)h * qtiles + qt) * keep : nullptr;
-  const int nsub = kSparse ? 2 * keep : (N + kBN - 1) / kBN;
+  const int nsub = kSparse ? (kTile / kBN) * keep : (N + kBN - 1) / kBN;
   auto kv_start = [&](int it) -> int {
     if (!kSparse) return it * kBN;
-    int t = irow[it >> 1];
+    int t = irow[it / (kTile / kBN)];
     t = t < 0 ? 0 : (t >= qtiles ? qtiles - 1 : t);
-    return t * kTile + (it & 1) * kBN;
+    return t * kTile + (it % (kTile / kBN)) * kBN;
   };
 
-  // Global -> register staging: K and V rows rg + 16 rr, 16-byte chunk ch.
-  const int ch = tid & 15, rg = tid >> 4;
-  u32x4 kr[4], vr[4];
-  auto load_kv = [&](int kv0) {
-    const int rem = (N - kv0) * kRowBytes;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * kHeadDim, rem);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)kv0 * kHeadDim, rem);
+  // Buffer-to-LDS loads: wave-wide load i of this wave fills LDS rows
+  // 4 (kLoadsPerWave wave + i) + (lane >> 4), 16-byte slot lane & 15; the lane
+  // fetches the global chunk that the swizzle places in that slot.
+  int koffg[kLoadsPerWave], voffg[kLoadsPerWave];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int off = (rg + 16 * rr) * kRowBytes + 16 * ch;
-      kr[rr] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-      vr[rr] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-    }
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int row = 4 * (kLoadsPerWave * wave + i) + (lane >> 4), slot = lane & 15;
+    koffg[i] = row * kRowBytes + ((slot ^ k_swz(row)) << 4);
+    voffg[i] = row * kRowBytes + ((slot ^ v_swz(row)) << 4);
+  }
+  auto load_k = [&](int kv0, auto bufc) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
+    unsigned char* dst = smem + decltype(bufc)::value * kTileBytes + wave * kLoadsPerWave * 1024;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, koffg[i], 0, 0, 0);
   };
-  auto store_kv = [&](auto bufc) {
-    unsigned char* Ks = smem + decltype(bufc)::value * kStage;
-    unsigned char* Vs = Ks + kKStage;
+  auto load_v = [&](int kv0, auto bufc) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
+    unsigned char* dst = smem + (2 + decltype(bufc)::value) * kTileBytes + wave * kLoadsPerWave * 1024;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = rg + 16 * rr;
-      *(u32x4*)(Ks + row * kRowBytes + ((ch ^ k_swz(row)) << 4)) = kr[rr];
-      *(u32x4*)(Vs + row * kRowBytes + ((ch ^ v_swz(row)) << 4)) = vr[rr];
-    }
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, voffg[i], 0, 0, 0);
   };
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
 
   // S^T operand: row key_of_row(l32) (+32 for the second 32-key block), chunk
-  // 2 dk + g; byte offsets within a stage, one per dk (the +32 rows and the
-  // stage are immediate offsets).
+  // 2 dk + g; byte offsets within a stage, one per dk.
   int koff[8];
   {
     const int krow = key_of_row(l32);
@@ -186,9 +197,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // V^T operand by transpose load: 16-lane group G = lane >> 4 covers head
   // dims 32 db + 16 (G & 1) + 0..15 and keys 32 kb + 16 (G >> 1) + 8 s + 0..7;
   // source lane s16 = lane & 15 reads 4 dims of key (s16 >> 2) (then + 4).
-  // Byte offsets within a stage, one per db; the key steps (32 kb + 8 s, and
-  // +4 for the second read) are whole rows and keep (key & 3), so they are
-  // immediate offsets.
+  // One byte offset per db; the key steps keep (key & 3) and are immediates.
   int voff[4];
   {
     const int s16 = lane & 15, G = lane >> 4;
@@ -197,120 +206,223 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int dim = vdim + 32 * db;
-      voff[db] = kKStage + vkey * kRowBytes + (((dim >> 3) ^ v_swz(vkey)) << 4) + 8 * ((dim >> 2) & 1);
+      voff[db] = vkey * kRowBytes + (((dim >> 3) ^ v_swz(vkey)) << 4) + 8 * ((dim >> 2) & 1);
     }
   }
 
-  auto compute = [&](auto bufc, int kv0) {
-    const unsigned char* st_base = smem + decltype(bufc)::value * kStage;
-    f32x16 s0, s1;
+  f32x16 oacc[kQB][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
-#pragma unroll
-    for (int dk = 0; dk < 8; ++dk) {
-      const bf16x8 a0 = *(const bf16x8*)(st_base + koff[dk]);
-      const bf16x8 a1 = *(const bf16x8*)(st_base + koff[dk] + 32 * kRowBytes);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[dk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[dk], s1, 0, 0, 0);
-    }
-    // s0[r] = S[q][kv0 + 16 g + r], s1[r] = S[q][kv0 + 32 + 16 g + r]
-    if (kv0 + kBN > N) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kv0 + 16 * g + r >= N) s0[r] = -INFINITY;
-        if (kv0 + 32 + 16 * g + r >= N) s1[r] = -INFINITY;
-      }
-    }
-    float mx = s0[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-    mx = halfwave_max(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_run));
-      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_run));
-      psum += s0[r] + s1[r];
-    }
-    l_run += psum;
-
-    bf16x8 p[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[0][i] = (__bf16)s0[i];
-      p[1][i] = (__bf16)s0[8 + i];
-      p[2][i] = (__bf16)s1[i];
-      p[3][i] = (__bf16)s1[8 + i];
-    }
-    // O^T += V^T P^T; step st = 2 kb + s covers keys 32 kb + 16 g + 8 s + 0..7
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const unsigned char* r0 = st_base + voff[db] + (32 * (st >> 1) + 8 * (st & 1)) * kRowBytes;
-        const unsigned char* r1 = r0 + 4 * kRowBytes;
-        const u32x2 lo =
-            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r0));
-        const u32x2 hi =
-            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r1));
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), p[st],
-                                                           oacc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  // One stage: prefetch stage it+1 into registers, multiply stage it out of
-  // LDS buffer `buf`, then park stage it+1 in the other buffer.  The loop is
-  // unrolled by two so the buffer (and every LDS address offset) is a constant.
-  auto step = [&](auto bufc, int it) {
-    constexpr int buf = decltype(bufc)::value;
-    const int kv0 = kv_start(it);
-    const bool more = it + 1 < nsub;
-    if (more) load_kv(kv_start(it + 1));
-    if (kv0 < N) compute(bufc, kv0);
-    if (more) store_kv(std::integral_constant<int, buf ^ 1>());
-    __syncthreads();
-  };
-  load_kv(kv_start(0));
-  store_kv(std::integral_constant<int, 0>());
-  __syncthreads();
-  for (int it = 0; it < nsub; it += 2) {
-    step(std::integral_constant<int, 0>(), it);
-    if (it + 1 < nsub) step(std::integral_constant<int, 1>(), it + 1);
-  }
-
-  // O^T accumulators: oacc[db][4 j + i] = O[q][32 db + 8 j + 4 g + i]
-  const float inv = 1.f / halfwave_sum(l_run);
-  if (qrow < N) {
-    uint16_t* orow = O + hoff + (size_t)qrow * kHeadDim;
+  for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const __bf16 b0 = (__bf16)(oacc[db][4 * j + 0] * inv);
-        const __bf16 b1 = (__bf16)(oacc[db][4 * j + 1] * inv);
-        const __bf16 b2 = (__bf16)(oacc[db][4 * j + 2] * inv);
-        const __bf16 b3 = (__bf16)(oacc[db][4 * j + 3] * inv);
-        u32x2 w;
-        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(u32x2*)(orow + 32 * db + 8 * j + 4 * g) = w;
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+  float m_run[kQB], l_run[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+
+  // S^T of one stage: S[qb][kb][r] = S[q0 + 32 qb + l32][kv0 + 32 kb + 16 g + r]
+  auto qk = [&](auto bufc, f32x16 (&S)[kQB][kKB]) {
+    const unsigned char* kb0 = smem + decltype(bufc)::value * kTileBytes;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kb0 + koff[dk] + kb * 32 * kRowBytes);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][dk], S[qb][kb], 0, 0, 0);
       }
+  };
+  // Keys past N: -inf scores.  Only stages that reach past the end need it.
+  auto mask = [&](f32x16 (&S)[kQB][kKB], int kv0) {
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv0 + 32 * kb + 16 * g + r >= N) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) S[qb][kb][r] = -INFINITY;
+        }
+  };
+  // Row max of a stage, in scaled log2 units.
+  auto rowmax = [&](const f32x16 (&S)[kQB][kKB], float (&mx)[kQB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float m = S[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, S[qb][kb][r]);
+      mx[qb] = halfwave_max(m) * c;
+    }
+  };
+  // Raise the running max (and rescale O and the sums) when some row of the
+  // wave exceeds it by more than 2^8.
+  auto maybe_rescale = [&](const float (&mx)[kQB]) {
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) up |= mx[qb] > m_run[qb] + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mx[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);   // 0 on the first stage
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+      }
+    }
+  };
+  // P = exp2(S c - m) as bf16 B-operands; P[qb][st] covers keys 32 kb + 16 g + 8 s + 0..7
+  // with st = 2 kb + s.
+  auto softmax = [&](const f32x16 (&S)[kQB][kKB], bf16x8 (&P)[kQB][2 * kKB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[qb][kb][r], c, -m_run[qb]));
+          ps[r & 1] += p;
+          P[qb][2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        }
+      l_run[qb] += ps[0] + ps[1];
+    }
+  };
+  // O^T += V^T P^T for one stage.
+  auto pv = [&](auto bufc, const bf16x8 (&P)[kQB][2 * kKB]) {
+    const unsigned char* vb0 = smem + (2 + decltype(bufc)::value) * kTileBytes;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int st = 0; st < 2 * kKB; ++st) {
+        const unsigned char* r0 = vb0 + voff[db] + (32 * (st >> 1) + 8 * (st & 1)) * kRowBytes;
+        const u32x2 lo =
+            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r0));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 4 * kRowBytes)));
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[qb][st], oacc[qb][db], 0, 0, 0);
+      }
+  };
+
+  f32x16 SA[kQB][kKB], SB[kQB][kKB];
+  bf16x8 P[kQB][2 * kKB];
+
+  // Stage `it`: its scores are in Scur (max already folded into m_run); K(it+1)
+  // is in K buffer b^1 and V(it) in V buffer b, b = it & 1.  Two scheduling
+  // regions: (1) softmax of stage it on the vector ALU interleaved with the
+  // S^T MFMAs of stage it+1 (into Snext), (2) the PV MFMAs of stage it
+  // interleaved with the row max of stage it+1.  On the last stage the S^T
+  // product reads a stale buffer and its result is discarded.
+  auto stage = [&](auto bufc, int it, f32x16 (&Scur)[kQB][kKB], f32x16 (&Snext)[kQB][kKB]) {
+    constexpr int b = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    const bool has_next = it + 1 < nsub;
+    const int kv_next = has_next ? kv_start(it + 1) : 0;
+    if (it + 2 < nsub) load_k(kv_start(it + 2), Buf<b>());
+    if (has_next) load_v(kv_next, Buf<b ^ 1>());
+
+    softmax(Scur, P);
+    qk(Buf<b ^ 1>(), Snext);
+    // Region 1: one K-operand read per (dk, kb) feeds kQB MFMAs; the softmax's
+    // ~56 kQB kKB VALU instructions are spread between the MFMAs.  Reads run
+    // one operand ahead.
+    {
+      constexpr int kOps = 8 * kKB, kValuPerMfma = (56 * kKB * kQB + kOps * kQB - 1) / (kOps * kQB);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int o = 0; o < kOps; ++o) {
+        if (o + 1 < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+        }
+      }
+    }
+
+    if (has_next && kv_next + kBN > N) mask(Snext, kv_next);
+
+    float mx[kQB];
+    pv(Buf<b>(), P);
+    rowmax(Snext, mx);
+    // Region 2: two transpose reads per (db, st) V operand feed kQB MFMAs; the
+    // row max of the next stage fills the gaps.  Reads run one operand ahead.
+    {
+      constexpr int kOps = 4 * 2 * kKB;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+      for (int o = 0; o < kOps; ++o) {
+        if (o + 1 < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+        }
+      }
+    }
+
+    if (has_next) maybe_rescale(mx);
+  };
+
+  // prologue: K(0), V(0), K(1) in flight, scores and max of stage 0
+  {
+    const int kv0 = kv_start(0);
+    load_k(kv0, Buf<0>());
+    load_v(kv0, Buf<0>());
+    if (nsub > 1) load_k(kv_start(1), Buf<1>());
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    qk(Buf<0>(), SA);
+    if (kv0 + kBN > N) mask(SA, kv0);
+    float mx[kQB];
+    rowmax(SA, mx);
+    maybe_rescale(mx);
+  }
+  for (int it = 0; it < nsub; it += 2) {
+    stage(Buf<0>(), it, SA, SB);
+    if (it + 1 < nsub) stage(Buf<1>(), it + 1, SB, SA);
+  }
+
+  // O^T accumulators: oacc[qb][db][4 j + i] = O[q0 + 32 qb + l32][32 db + 8 j + 4 g + i]
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float inv = 1.f / halfwave_sum(l_run[qb]);
+    const int qrow = q0 + 32 * qb + l32;
+    if (qrow < N) {
+      uint16_t* orow = O + hoff + (size_t)qrow * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const __bf16 b0 = (__bf16)(oacc[qb][db][4 * j + 0] * inv);
+          const __bf16 b1 = (__bf16)(oacc[qb][db][4 * j + 1] * inv);
+          const __bf16 b2 = (__bf16)(oacc[qb][db][4 * j + 2] * inv);
+          const __bf16 b3 = (__bf16)(oacc[qb][db][4 * j + 3] * inv);
+          u32x2 w;
+          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          *(u32x2*)(orow + 32 * db + 8 * j + 4 * g) = w;
+        }
+    }
   }
 }
 
