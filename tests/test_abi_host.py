@@ -39,6 +39,12 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == set(fv.SIGNATURES)
 
 
+def test_library_resolves_every_symbol_at_load():
+    # a kernel whose host stub was not emitted shows up as an unresolved symbol;
+    # RTLD_NOW makes the loader resolve everything instead of on first call
+    ctypes.CDLL(fv.LIB_PATH, mode=os.RTLD_NOW)
+
+
 def test_status_strings(lib):
     for s in range(0, 6):
         assert fv.status_string(s)

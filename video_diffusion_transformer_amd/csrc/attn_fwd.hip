@@ -63,20 +63,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBM = 128;                    // query rows per workgroup
-constexpr int kBN = 64;                     // keys per LDS stage
-constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
-constexpr int kQB = 1;                      // 32-row query blocks per wave
-constexpr int kWaves = kBM / (32 * kQB);    // 4 waves of 32 query rows
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = kHeadDim * 2;     // 256 B per token row
-constexpr int kTileBytes = kBN * kRowBytes; // 16 KiB: one K or V stage
-constexpr int kLds = 4 * kTileBytes;        // K[2], V[2]: 64 KiB, two workgroups per CU
-constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
 constexpr int kXcds = 8;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
-constexpr int kWaitVmcnt0 = 0x0F70;         // s_waitcnt vmcnt(0), other counters untouched
+// s_waitcnt immediates: vmcnt in bits 3:0, expcnt 6:4 (7 = no wait), lgkmcnt
+// 11:8.  kWaitVm(n) waits until at most n buffer loads are in flight and every
+// LDS access has completed.
+constexpr int kWaitVmcnt0 = 0x0070;
+constexpr int kWaitVm(int n) { return kWaitVmcnt0 | n; }
 
 // K rows: chunk (16 B) swizzle; the 16 rows read by lanes 0..15 (and by 16..31)
 // of one S^T operand load land on 16 distinct chunk positions.
@@ -119,12 +114,31 @@ __device__ __forceinline__ float halfwave_sum(float x) {
 template <int B>
 using Buf = std::integral_constant<int, B>;
 
-template <bool kSparse>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, const int32_t* __restrict__ idx,
-    int keep, int N, int qtiles, float c) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+// kWaves waves of 32 query rows (a workgroup covers kBM = 32 kWaves rows) and
+// kStages LDS slots for each of K and V (loads run kStages - 1 stages ahead).
+// The body lives in a __device__ template so that only the device compilation
+// instantiates it; the __global__ wrapper below is all the host side sees.
+template <bool kSparse, int kWaves, int kStages, int kQB, int kBN>
+__device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
+                                              const uint16_t* __restrict__ K,
+                                              const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                              const int32_t* __restrict__ idx, int keep, int N,
+                                              int qtiles, float c) {
+  constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
+  constexpr int kTileBytes = kBN * kRowBytes; // one K or V stage
+  constexpr int kBM = 32 * kQB * kWaves;
+  constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
+  constexpr int kPrefetch = kStages - 1;
+  static_assert(!kSparse || kBM == kTile, "sparse workgroups cover one selection tile");
+  // One LDS array per slot: distinct objects let the compiler see that a read
+  // of one slot cannot alias a buffer-to-LDS load still landing in another,
+  // so it does not wait for every load in flight before each LDS read.
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[kTileBytes], k_lds1[kTileBytes],
+      k_lds2[kStages > 2 ? kTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[kTileBytes], v_lds1[kTileBytes],
+      v_lds2[kStages > 2 ? kTileBytes : 16];
+  unsigned char* const k_slots[3] = {k_lds0, k_lds1, k_lds2};
+  unsigned char* const v_slots[3] = {v_lds0, v_lds1, v_lds2};
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int h = L / qtiles, qt = L - h * qtiles;
@@ -173,14 +187,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   auto load_k = [&](int kv0, auto bufc) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
-    unsigned char* dst = smem + decltype(bufc)::value * kTileBytes + wave * kLoadsPerWave * 1024;
+    unsigned char* dst = k_slots[decltype(bufc)::value] + wave * kLoadsPerWave * 1024;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, koffg[i], 0, 0, 0);
   };
   auto load_v = [&](int kv0, auto bufc) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Vh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
-    unsigned char* dst = smem + (2 + decltype(bufc)::value) * kTileBytes + wave * kLoadsPerWave * 1024;
+    unsigned char* dst = v_slots[decltype(bufc)::value] + wave * kLoadsPerWave * 1024;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, voffg[i], 0, 0, 0);
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // S^T of one stage: S[qb][kb][r] = S[q0 + 32 qb + l32][kv0 + 32 kb + 16 g + r]
   auto qk = [&](auto bufc, f32x16 (&S)[kQB][kKB]) {
-    const unsigned char* kb0 = smem + decltype(bufc)::value * kTileBytes;
+    const unsigned char* kb0 = k_slots[decltype(bufc)::value];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   // O^T += V^T P^T for one stage.
   auto pv = [&](auto bufc, const bf16x8 (&P)[kQB][2 * kKB]) {
-    const unsigned char* vb0 = smem + (2 + decltype(bufc)::value) * kTileBytes;
+    const unsigned char* vb0 = v_slots[decltype(bufc)::value];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -323,23 +337,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 SA[kQB][kKB], SB[kQB][kKB];
   bf16x8 P[kQB][2 * kKB];
 
-  // Stage `it`: its scores are in Scur (max already folded into m_run); K(it+1)
-  // is in K buffer b^1 and V(it) in V buffer b, b = it & 1.  Two scheduling
-  // regions: (1) softmax of stage it on the vector ALU interleaved with the
-  // S^T MFMAs of stage it+1 (into Snext), (2) the PV MFMAs of stage it
-  // interleaved with the row max of stage it+1.  On the last stage the S^T
-  // product reads a stale buffer and its result is discarded.
-  auto stage = [&](auto bufc, int it, f32x16 (&Scur)[kQB][kKB], f32x16 (&Snext)[kQB][kKB]) {
-    constexpr int b = decltype(bufc)::value;
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+  // Stage `it` (k = it mod kUnroll): its scores are in Scur (max already
+  // folded into m_run); K(it+1) is in K slot (k+1) mod kStages and V(it) in V
+  // slot k mod kStages.  It starts K(it+kStages) and V(it+kStages-1) into the
+  // slots stage it-1 finished with.  Two scheduling regions: (1) softmax of
+  // stage it on the vector ALU interleaved with the S^T MFMAs of stage it+1
+  // (into Snext), (2) the PV MFMAs of stage it interleaved with the row max of
+  // stage it+1.  On the last stage the S^T product reads a stale slot and its
+  // result is discarded.
+  auto loads_at = [&](int i) {   // wave-wide loads a stage issues (uniform)
+    return (i + kStages < nsub ? kLoadsPerWave : 0) + (i + kPrefetch < nsub ? kLoadsPerWave : 0);
+  };
+  auto stage = [&](auto kc, int it, f32x16 (&Scur)[kQB][kKB], f32x16 (&Snext)[kQB][kKB]) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int kSlotK = (k + 1) % kStages, kSlotV = k % kStages;
+    // K(it+1) and V(it) were started kPrefetch stages ago; only the loads of
+    // the stages after that may still be in flight.
+    const int newer = (kPrefetch >= 2 && it >= 1) ? loads_at(it - 1) : 0;
+    if (newer == 2 * kLoadsPerWave)
+      __builtin_amdgcn_s_waitcnt(kWaitVm(2 * kLoadsPerWave));
+    else if (newer == kLoadsPerWave)
+      __builtin_amdgcn_s_waitcnt(kWaitVm(kLoadsPerWave));
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm(0));
+    // A bare barrier: the waits above cover every load this stage reads, and
+    // every LDS read of the previous stage has completed (its results were
+    // consumed), so no wave can still be reading the slots refilled below.
+    __builtin_amdgcn_s_barrier();
     const bool has_next = it + 1 < nsub;
     const int kv_next = has_next ? kv_start(it + 1) : 0;
-    if (it + 2 < nsub) load_k(kv_start(it + 2), Buf<b>());
-    if (has_next) load_v(kv_next, Buf<b ^ 1>());
+    if (it + kStages < nsub) load_k(kv_start(it + kStages), Buf<k % kStages>());
+    if (it + kPrefetch < nsub) load_v(kv_start(it + kPrefetch), Buf<(k + kStages - 1) % kStages>());
 
     softmax(Scur, P);
-    qk(Buf<b ^ 1>(), Snext);
+    qk(Buf<kSlotK>(), Snext);
     // Region 1: one K-operand read per (dk, kb) feeds kQB MFMAs; the softmax's
     // ~56 kQB kKB VALU instructions are spread between the MFMAs.  Reads run
     // one operand ahead.
@@ -360,7 +391,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (has_next && kv_next + kBN > N) mask(Snext, kv_next);
 
     float mx[kQB];
-    pv(Buf<b>(), P);
+    pv(Buf<kSlotV>(), P);
     rowmax(Snext, mx);
     // Region 2: two transpose reads per (db, st) V operand feed kQB MFMAs; the
     // row max of the next stage fills the gaps.  Reads run one operand ahead.
@@ -381,23 +412,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (has_next) maybe_rescale(mx);
   };
 
-  // prologue: K(0), V(0), K(1) in flight, scores and max of stage 0
+  // prologue: K(0..kStages-1) and V(0..kStages-2) started, scores and max of stage 0
   {
     const int kv0 = kv_start(0);
     load_k(kv0, Buf<0>());
+    if (1 < nsub) load_k(kv_start(1), Buf<1 % kStages>());
+    if (kStages > 2 && 2 < nsub) load_k(kv_start(2), Buf<2 % kStages>());
     load_v(kv0, Buf<0>());
-    if (nsub > 1) load_k(kv_start(1), Buf<1>());
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    if (kStages > 2 && 1 < nsub) load_v(kv_start(1), Buf<1 % kStages>());
+    __builtin_amdgcn_s_waitcnt(kWaitVm(0));
+    __builtin_amdgcn_s_barrier();
     qk(Buf<0>(), SA);
     if (kv0 + kBN > N) mask(SA, kv0);
     float mx[kQB];
     rowmax(SA, mx);
     maybe_rescale(mx);
   }
-  for (int it = 0; it < nsub; it += 2) {
+  // Unrolled so that every slot and score register set is a constant.
+  constexpr int kUnroll = kStages % 2 ? 2 * kStages : kStages;
+  for (int it = 0; it < nsub; it += kUnroll) {
     stage(Buf<0>(), it, SA, SB);
     if (it + 1 < nsub) stage(Buf<1>(), it + 1, SB, SA);
+    if (kUnroll > 2 && it + 2 < nsub) stage(Buf<2 % kUnroll>(), it + 2, SA, SB);
+    if (kUnroll > 3 && it + 3 < nsub) stage(Buf<3 % kUnroll>(), it + 3, SB, SA);
+    if (kUnroll > 4 && it + 4 < nsub) stage(Buf<4 % kUnroll>(), it + 4, SA, SB);
+    if (kUnroll > 5 && it + 5 < nsub) stage(Buf<5 % kUnroll>(), it + 5, SB, SA);
   }
 
   // O^T accumulators: oacc[qb][db][4 j + i] = O[q0 + 32 qb + l32][32 db + 8 j + 4 g + i]
@@ -426,21 +465,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// kQB = 1: 32 query rows per wave, two waves per SIMD (256 registers each);
+// kQB = 2: 64 rows per wave, one wave per SIMD with the whole register file.
+template <bool kSparse, int kWaves, int kStages, int kQB, int kBN>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3 - kQB, 3 - kQB))) void
+attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                const int32_t* __restrict__ idx, int keep, int N, int qtiles, float c) {
+  attn_fwd_body<kSparse, kWaves, kStages, kQB, kBN>(Q, K, V, O, idx, keep, N, qtiles, c);
+}
+
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             uint16_t* out, const int32_t* idx, int keep, int heads, int tokens,
                             float scale, hipStream_t stream) {
-  const int qtiles = (tokens + kBM - 1) / kBM;
-  const long long blocks = (long long)heads * qtiles;
-  if (blocks <= 0) return hipSuccess;
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  if (idx)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
-                       k, v, out, idx, keep, tokens, qtiles, c);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q,
-                       k, v, out, idx, keep, tokens, qtiles, c);
+  if (idx) {
+    // one 128-row selection tile per workgroup (4 waves), 2 workgroups per CU
+    const int qtiles = (tokens + kTile - 1) / kTile;
+    const long long blocks = (long long)heads * qtiles;
+    if (blocks <= 0) return hipSuccess;
+    attn_fwd_kernel<true, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        q, k, v, out, idx, keep, tokens, qtiles, c);
+  } else {
+    // 256 query rows per workgroup (8 waves) share each K/V stage; one
+    // workgroup per CU leaves LDS for three slots, loads two stages ahead
+    const int qtiles = (tokens + 255) / 256;
+    const long long blocks = (long long)heads * qtiles;
+    if (blocks <= 0) return hipSuccess;
+    attn_fwd_kernel<false, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+        q, k, v, out, idx, keep, tokens, qtiles, c);
+  }
   return hipGetLastError();
 }
 
