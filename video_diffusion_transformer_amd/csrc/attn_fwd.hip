@@ -36,7 +36,9 @@
 //   scores alternate between two register sets across the two unrolled stages,
 //   so the softmax of one stage and the S^T product of the next never touch
 //   the same registers.  One barrier per stage; the loads of K(j+2) and V(j+1)
-//   are in flight for the whole stage.
+//   are in flight for the whole stage.  The wave raises its issue priority for
+//   the PV region, so a SIMD shared with a wave in its softmax keeps the matrix
+//   pipe busy.
 // * fp32 online softmax in the exp2 domain (scale * log2 e folded into one
 //   FMA per score).  The running max is only raised, and O and the running sum
 //   rescaled, when some row of the wave sees a score more than 2^8 above it
@@ -391,6 +393,9 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     if (has_next && kv_next + kBN > N) mask(Snext, kv_next);
 
     float mx[kQB];
+    // Raise this wave's issue priority for the MFMA-heavy PV region: when the
+    // other wave on the SIMD is in its softmax, the matrix pipe stays fed.
+    __builtin_amdgcn_s_setprio(1);
     pv(Buf<kSlotV>(), P);
     rowmax(Snext, mx);
     // Region 2: two transpose reads per (db, st) V operand feed kQB MFMAs; the
@@ -409,6 +414,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) maybe_rescale(mx);
   };
 
