@@ -5,8 +5,10 @@ cpu_baseline leg of bench.py, never by the library or its binding.
 """
 
 from .attention import (TILE, attention_rows, dense, keep_count, kept_keys, select_tiles,
-                        sparse, tile_count, tile_means, tile_scores, top_tiles)
+                        sparse, tile_count, tile_means, tile_scores, top_tiles, window_attention,
+                        window_frames_allowed, window_tiles)
 from .widen import widen
 
 __all__ = ["TILE", "attention_rows", "dense", "keep_count", "kept_keys", "select_tiles",
-           "sparse", "tile_count", "tile_means", "tile_scores", "top_tiles", "widen"]
+           "sparse", "tile_count", "tile_means", "tile_scores", "top_tiles", "widen",
+           "window_attention", "window_frames_allowed", "window_tiles"]

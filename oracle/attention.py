@@ -30,7 +30,13 @@ Sources (the pages are the authority on what is computed):
   (FastH3 page, "Lever two": the base loader zero-initializes
   ``to_gate_compress``).  Softmax is normalized over the kept keys only.
 
-Parity pins for every function live in tests/test_oracle_pins.py.
+* Windowed softmax (the softmax branch of Video DeltaNet): exact attention
+  restricted to a window of latent-frame chunks plus two anchor frames
+  (FreeVideo page, section "Where Video DeltaNet comes in"); see the readings
+  at ``window_frames_allowed``.
+
+Parity pins for every function live in tests/test_oracle_pins.py and
+tests/test_oracle_window.py.
 """
 
 from __future__ import annotations
@@ -180,5 +186,70 @@ def sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, idx: np.nd
         for t in np.unique(tile_of):
             sel = np.nonzero(tile_of == t)[0]
             keys = kept_keys(idx[h, t], N)
+            out[h, sel] = attention_rows(q[h, rows[sel]], k[h, keys], v[h, keys], scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# windowed softmax of Video DeltaNet's softmax branch (definition)
+#
+# FreeVideo page, section "Where Video DeltaNet comes in": softmax stays exact
+# but only inside a window; each query chunk of five latent frames sees itself
+# and its neighbouring chunk on each side (a 15-frame window); every frame also
+# sees the first and the last latent frame, and those two frames see every
+# frame.  Readings taken here: latent frame of token i = i // frame_tokens;
+# chunk of frame f = f // chunk_frames, counted from frame 0 (the last chunk
+# may be short); "neighbours" chunks on each side.
+# --------------------------------------------------------------------------
+
+def window_frames_allowed(frames: int, chunk_frames: int = 5, neighbours: int = 1) -> np.ndarray:
+    """Boolean [F, F]: may a query in frame qf attend to a key in frame kf."""
+    f = np.arange(frames)
+    chunk = f // chunk_frames
+    allowed = np.abs(chunk[:, None] - chunk[None, :]) <= neighbours
+    if frames:
+        for anchor in (0, frames - 1):
+            allowed[:, anchor] = True
+            allowed[anchor, :] = True
+    return allowed
+
+
+def window_tiles(tokens: int, frame_tokens: int, chunk_frames: int = 5, neighbours: int = 1):
+    """Key tiles each 128-token query tile must visit: every key tile holding a
+    key that some query of the tile may attend to.  Returns (idx [T, T] int32,
+    padded with -1, ascending; count [T] int32)."""
+    T = tile_count(tokens)
+    frames = -(-tokens // frame_tokens)
+    allowed = window_frames_allowed(frames, chunk_frames, neighbours)
+    token_frame = np.arange(tokens) // frame_tokens
+    idx = np.full((T, T), -1, dtype=np.int32)
+    count = np.zeros(T, dtype=np.int32)
+    for t in range(T):
+        qframes = np.unique(token_frame[t * TILE:min(t * TILE + TILE, tokens)])
+        kframes = np.nonzero(allowed[qframes].any(axis=0))[0]
+        key_ok = np.isin(token_frame, kframes)
+        tiles = np.unique(np.nonzero(key_ok)[0] // TILE)
+        idx[t, :len(tiles)] = tiles
+        count[t] = len(tiles)
+    return idx, count
+
+
+def window_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, frame_tokens: int,
+                     chunk_frames: int = 5, neighbours: int = 1, rows=None) -> np.ndarray:
+    """Softmax attention restricted to the window and anchor frames, per head.
+
+    q, k, v: [H, N, d] float64.  ``rows`` as in ``dense``.
+    """
+    H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    frames = -(-N // frame_tokens)
+    allowed = window_frames_allowed(frames, chunk_frames, neighbours)
+    token_frame = np.arange(N) // frame_tokens
+    out = np.empty((H, len(rows), d), dtype=np.float64)
+    qframe = token_frame[rows]
+    for h in range(H):
+        for f in np.unique(qframe):
+            sel = np.nonzero(qframe == f)[0]
+            keys = np.nonzero(allowed[f, token_frame])[0]
             out[h, sel] = attention_rows(q[h, rows[sel]], k[h, keys], v[h, keys], scale)
     return out
