@@ -35,6 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_dense_72576x56_traffic.json"
 KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", "attn_fwd.hip")
 
 TOKENS, HEADS, GROUP, KEEP_FRAC, SEED = 72576, 56, 16, 0.1, 3
+FRAME_TOKENS = 1008   # latent tokens per frame at 1344x768
 
 
 def log(*a):
@@ -54,6 +55,19 @@ def sparse_flops(idx, tokens: int, d: int = 128) -> float:
     valid[-1] = tokens - 128 * (T - 1)
     keys = valid[idx].sum(axis=2)            # [H, T] keys seen by each query tile
     return float(4 * d * (keys * valid[None, :]).sum())
+
+
+def window_flops(tokens: int, frame_tokens: int, chunk: int, nb: int, heads: int, d: int = 128) -> float:
+    """QK^T + PV FLOPs over the (query, key) pairs the frame window allows."""
+    import numpy as np
+    frames = -(-tokens // frame_tokens)
+    f = np.arange(frames)
+    allowed = np.abs(f[:, None] // chunk - f[None, :] // chunk) <= nb
+    allowed[:, [0, frames - 1]] = True
+    allowed[[0, frames - 1], :] = True
+    per_frame = np.minimum(frame_tokens, tokens - f * frame_tokens).astype(np.float64)
+    pairs = float(per_frame @ allowed.astype(np.float64) @ per_frame)
+    return 4.0 * d * heads * pairs
 
 
 def cpu_baseline(q, k, v, scale, budget_s: float):
@@ -100,8 +114,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse"], default=None,
-                    help="time only one of the two modes (for profiler runs; value then covers that mode)")
+    ap.add_argument("--only", choices=["dense", "sparse", "window"], default=None,
+                    help="time only one mode (for profiler runs; value then covers that mode, "
+                         "0 for window, which is timed outside the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration runs)")
     args = ap.parse_args()
@@ -150,6 +165,7 @@ def main():
 
     do_dense = args.only in (None, "dense")
     do_sparse = args.only in (None, "sparse")
+    do_window = args.only in (None, "window")
     if not do_dense:
         flop_dense = 0.0
     if not do_sparse:
@@ -199,6 +215,33 @@ def main():
         torch.cuda.synchronize()
         sel_ms.append(sel_ev[0].elapsed_time(sel_ev[1]))
 
+    # frame-window softmax (Video DeltaNet's softmax branch), outside the step:
+    # 5-frame chunks, one neighbouring chunk on each side, first and last frame
+    # as anchors; all 56 heads in one launch
+    window = None
+    if do_window:
+        out_window = torch.empty_like(qd)
+        w_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        w_ms = []
+        for i in range(4):
+            w_ev[0].record(stream)
+            fv.forward_window(qd, kd, vd, frame_tokens=FRAME_TOKENS, chunk_frames=5, neighbours=1,
+                              scale=scale, out=out_window)
+            w_ev[1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                w_ms.append(w_ev[0].elapsed_time(w_ev[1]))
+        del out_window
+        wm = float(np.median(w_ms))
+        flop_w = window_flops(TOKENS, FRAME_TOKENS, 5, 1, HEADS)
+        idx_w, cnt_w = fv.window_tiles(TOKENS, FRAME_TOKENS, 5, 1, device=dev)
+        flop_w_visited = 4.0 * 128 * HEADS * 128 * 128 * float(cnt_w.sum().item())
+        del idx_w, cnt_w
+        window = {"ms": round(wm, 3), "flop_allowed": flop_w,
+                  "tflops_effective": round(flop_w / (wm * 1e-3) / 1e12, 2),
+                  "tflops_visited": round(flop_w_visited / (wm * 1e-3) / 1e12, 2),
+                  "density": round(flop_w / (4.0 * TOKENS * TOKENS * 128 * HEADS), 4)}
+
     d_ms = float(np.median(dense_ms))
     s_ms = float(np.median(sparse_ms))
     dense_tflops = flop_dense / max(d_ms * 1e-3, 1e-12) / 1e12
@@ -219,7 +262,7 @@ def main():
         pass
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_fwd_kernel<false, 8, 2, 1, 64> (dense)",
+                "traffic": traffic, "kernel": "attn_fwd_kernel<0, 8, 2, 1, 64> (dense)",
                 "avg_launch_ms": round(dense_launch_ms, 4)}
 
     result = {
@@ -247,6 +290,10 @@ def main():
                    "speedup_vs_dense": round(d_ms / s_ms, 3) if do_dense and do_sparse else None},
         "roofline": roofline,
     }
+    if window is not None:
+        if do_dense:
+            window["speedup_vs_dense"] = round(d_ms / window["ms"], 3)
+        result["window"] = window
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), budget", args.cpu_budget, "s")
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)

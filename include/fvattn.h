@@ -129,6 +129,27 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
                          int group_heads, int tokens, int head_dim, float scale, int mode,
                          double keep_frac, void* stream);
 
+/* Frame-window softmax, the softmax branch of Video DeltaNet (FreeVideo page,
+ * section "Where Video DeltaNet comes in"): exact softmax attention in which
+ * a query of latent frame qf sees a key of latent frame kf only if
+ * |qf / chunk_frames - kf / chunk_frames| <= neighbours (integer division;
+ * chunks counted from frame 0) or kf or qf is the first or the last frame.
+ * Latent frame of token i = i / frame_tokens (1,008 at 1344x768; chunks of 5
+ * frames with 1 neighbour on each side give the page's 15-frame window).
+ * q, k, v, out as in fvattn_forward.  frame_tokens >= 64 (else
+ * FVATTN_ERR_UNSUPPORTED), chunk_frames >= 1, neighbours >= 0.  Uses
+ * stream-ordered scratch for the key-tile lists (T*T + T int32). */
+int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
+                          int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,
+                          int neighbours, void* stream);
+
+/* The key-tile lists fvattn_forward_window walks: for each 128-token query
+ * tile t, the ascending indices of the key tiles holding at least one key that
+ * some query of t may attend to.  idx_out: int32 [T][T] device, row t holds
+ * count_out[t] indices followed by -1; count_out: int32 [T] device. */
+int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neighbours,
+                        int32_t* idx_out, int32_t* count_out, void* stream);
+
 /* Step S1 alone, for checking: fp64 tile means of x, bf16 [heads][tokens][128]
  * in, means_out fp64 [heads][T][128] out (device pointers). */
 int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double* means_out,

@@ -174,3 +174,46 @@ def test_binding_rejects_cpu_tensors():
         fv.forward(q, q, q)
     with pytest.raises(TypeError):
         fv.forward(q.float(), q.float(), q.float())
+
+
+def _win(lib, q=BOGUS, k=BOGUS, v=BOGUS, o=BOGUS, heads=4, tokens=1008 * 12, hd=128, scale=0.088,
+         ft=1008, chunk=5, nb=1):
+    return lib.fvattn_forward_window(q, k, v, o, heads, tokens, hd, scale, ft, chunk, nb, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(o=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(heads=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(tokens=-5), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(chunk=0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(nb=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(hd=64), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(ft=63), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(ft=0), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(tokens=2049 * 128), fv.FVATTN_ERR_UNSUPPORTED),
+])
+def test_forward_window_rejects_bad_arguments(lib, kw, want):
+    assert _win(lib, **kw) == want
+
+
+def test_window_entry_points_empty_and_bad(lib):
+    assert _win(lib, q=NULL, k=NULL, v=NULL, o=NULL, heads=0) == fv.FVATTN_OK
+    assert _win(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0) == fv.FVATTN_OK
+    wt = lib.fvattn_window_tiles
+    assert wt(0, 1008, 5, 1, NULL, NULL, NULL) == fv.FVATTN_OK
+    assert wt(-1, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 1008, 0, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 1008, 5, -1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 32, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert wt(5000, 1008, 5, 1, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 1008, 5, 1, BOGUS, NULL, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(2049 * 128, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+
+
+def test_window_alloc_failure_hook(lib, monkeypatch):
+    monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
+    assert _win(lib) == fv.FVATTN_ERR_ALLOC
+    assert _win(lib, q=NULL) == fv.FVATTN_ERR_INVALID_ARG

@@ -219,6 +219,41 @@ def test_head_groups_equal_one_launch_bitwise():
             assert torch.equal(whole, grouped), (mode, g)
 
 
+# ------------------------------------------------------------------ frame window (Video DeltaNet's softmax branch)
+
+@pytest.mark.parametrize("N,ft,chunk,nb", [(1, 64, 5, 1), (64, 64, 5, 1), (1000, 64, 2, 1), (900, 100, 3, 1),
+                                           (1300, 130, 2, 0), (128, 128, 5, 1), (5040, 1008, 5, 1),
+                                           (20000, 64, 1, 0), (72576, 1008, 5, 1), (102816, 1008, 5, 1),
+                                           (72576, 1008, 5, 20)])
+def test_window_tiles_bit_exact(N, ft, chunk, nb):
+    say("window tiles", N, ft, chunk, nb)
+    idx, count = fv.window_tiles(N, ft, chunk, nb, device=DEV)
+    ref_idx, ref_count = oracle.window_tiles(N, ft, chunk, nb)
+    assert np.array_equal(count.cpu().numpy(), ref_count)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+@pytest.mark.parametrize("N,ft,chunk,nb,dist", [(700, 64, 2, 1, "iid"), (1000, 100, 3, 1, "iid"),
+                                                (2000, 64, 1, 0, "iid"), (1300, 130, 2, 0, "iid"),
+                                                (5040, 1008, 1, 0, "frame"), (5040, 1008, 5, 1, "frame"),
+                                                (4100, 200, 2, 1, "frame"), (64, 64, 5, 1, "iid"),
+                                                (70, 64, 1, 0, "iid")])
+def test_window_attention_matches_oracle(N, ft, chunk, nb, dist):
+    say("window attention", N, ft, chunk, nb, dist)
+    q, k, v = inputs.make_qkv(N, 2, dist, 300 + N, frame_tokens=ft)
+    out = fv.forward_window(*to_dev(q, k, v), frame_tokens=ft, chunk_frames=chunk, neighbours=nb).cpu()
+    ref = oracle.window_attention(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128), ft, chunk, nb)
+    assert_close(oracle.widen(out), ref, f"window N={N} ft={ft} chunk={chunk} nb={nb}")
+
+
+@pytest.mark.parametrize("N,ft", [(5040, 1008), (1000, 64), (129, 64)])
+def test_window_covering_everything_is_dense_bitwise(N, ft):
+    q, k, v = to_dev(*inputs.make_qkv(N, 3, "frame", 80 + N))
+    a = fv.forward_window(q, k, v, frame_tokens=ft, chunk_frames=1, neighbours=N)
+    b = fv.forward(q, k, v, mode="dense")
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")
@@ -278,3 +313,26 @@ def test_config4_sparse_and_dense(cfg4):
 @pytest.mark.timeout(400)
 def test_config5_sparse_and_dense(cfg5):
     _full_size_sparse_and_dense(5, cfg5)
+
+
+def _full_size_window(cid, qkv):
+    c = inputs.CONFIGS[cid]
+    q, k, v = qkv
+    out = fv.forward_window(*to_dev(q, k, v), frame_tokens=1008, chunk_frames=5, neighbours=1,
+                            scale=c.scale)
+    rows = sample_rows(c.tokens, 24, 10 + cid)
+    heads = list(range(0, c.heads, 5)) + [c.heads - 1]
+    got = out[heads][:, rows].cpu()
+    qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
+    ref = oracle.window_attention(qw, kw, vw, c.scale, 1008, 5, 1, rows=rows)
+    assert_close(oracle.widen(got), ref, f"{c.name} window")
+
+
+@pytest.mark.timeout(300)
+def test_config4_window(cfg4):
+    _full_size_window(4, cfg4)
+
+
+@pytest.mark.timeout(300)
+def test_config5_window(cfg5):
+    _full_size_window(5, cfg5)

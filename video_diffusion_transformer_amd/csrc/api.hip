@@ -230,6 +230,61 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
   return FVATTN_OK;
 }
 
+int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neighbours,
+                        int32_t* idx_out, int32_t* count_out, void* stream) {
+  if (tokens < 0 || chunk_frames < 1 || neighbours < 0) return FVATTN_ERR_INVALID_ARG;
+  if (frame_tokens < 64) return FVATTN_ERR_UNSUPPORTED;
+  if (tokens == 0) return FVATTN_OK;
+  if (!idx_out || !count_out) return FVATTN_ERR_INVALID_ARG;
+  if (tiles_of(tokens) > FVATTN_MAX_TILES) return FVATTN_ERR_UNSUPPORTED;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  fvattn::WindowParams wp;
+  wp.frame_tokens = frame_tokens;
+  wp.chunk_frames = chunk_frames;
+  wp.neighbours = neighbours;
+  wp.frames = (tokens - 1) / frame_tokens + 1;
+  return hip_status(fvattn::launch_window_tiles(tokens, wp, idx_out, count_out, (hipStream_t)stream));
+}
+
+int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
+                          int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,
+                          int neighbours, void* stream) {
+  if (heads < 0 || tokens < 0 || !scale_ok(scale) || chunk_frames < 1 || neighbours < 0)
+    return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || frame_tokens < 64) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) return FVATTN_OK;
+  if (!q || !k || !v || !out) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead || tiles_of(tokens) > FVATTN_MAX_TILES)
+    return FVATTN_ERR_UNSUPPORTED;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = tiles_of(tokens);
+  void* scratch = nullptr;
+  const size_t idx_bytes = align256(sizeof(int32_t) * (size_t)T * T);
+  if (hipMallocAsync(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)T), st) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  int32_t* idx = (int32_t*)scratch;
+  int32_t* counts = (int32_t*)((char*)scratch + idx_bytes);
+  fvattn::WindowParams wp;
+  wp.counts = counts;
+  wp.frame_tokens = frame_tokens;
+  wp.chunk_frames = chunk_frames;
+  wp.neighbours = neighbours;
+  wp.frames = (tokens - 1) / frame_tokens + 1;
+  hipError_t e = fvattn::launch_window_tiles(tokens, wp, idx, counts, st);
+  if (e == hipSuccess)
+    e = fvattn::launch_attention_window((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                        (uint16_t*)out, idx, wp, heads, tokens, scale, st);
+  rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(scratch, st));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
 int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double* means_out,
                       void* stream) {
   if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;

@@ -120,18 +120,20 @@ using Buf = std::integral_constant<int, B>;
 // kStages LDS slots for each of K and V (loads run kStages - 1 stages ahead).
 // The body lives in a __device__ template so that only the device compilation
 // instantiates it; the __global__ wrapper below is all the host side sees.
-template <bool kSparse, int kWaves, int kStages, int kQB, int kBN>
+// kMode: 0 dense, 1 per-head kept-tile lists of `keep` tiles, 2 frame-window
+// lists shared by all heads (per-row counts, per-element frame mask).
+template <int kMode, int kWaves, int kStages, int kQB, int kBN>
 __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                                               const uint16_t* __restrict__ K,
                                               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                               const int32_t* __restrict__ idx, int keep, int N,
-                                              int qtiles, float c) {
+                                              int qtiles, float c, WindowParams wp) {
   constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
   constexpr int kTileBytes = kBN * kRowBytes; // one K or V stage
   constexpr int kBM = 32 * kQB * kWaves;
   constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
   constexpr int kPrefetch = kStages - 1;
-  static_assert(!kSparse || kBM == kTile, "sparse workgroups cover one selection tile");
+  static_assert(kMode == 0 || kBM == kTile, "tile-list workgroups cover one selection tile");
   // One LDS array per slot: distinct objects let the compiler see that a read
   // of one slot cannot alias a buffer-to-LDS load still landing in another,
   // so it does not wait for every load in flight before each LDS read.
@@ -168,10 +170,13 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       }
   }
 
-  const int32_t* irow = kSparse ? idx + ((size_t)h * qtiles + qt) * keep : nullptr;
-  const int nsub = kSparse ? (kTile / kBN) * keep : (N + kBN - 1) / kBN;
+  const int32_t* irow = kMode == 1   ? idx + ((size_t)h * qtiles + qt) * keep
+                        : kMode == 2 ? idx + (size_t)qt * qtiles
+                                     : nullptr;
+  const int nsub = kMode == 0 ? (N + kBN - 1) / kBN
+                              : (kTile / kBN) * (kMode == 1 ? keep : wp.counts[qt]);
   auto kv_start = [&](int it) -> int {
-    if (!kSparse) return it * kBN;
+    if (kMode == 0) return it * kBN;
     int t = irow[it / (kTile / kBN)];
     t = t < 0 ? 0 : (t >= qtiles ? qtiles - 1 : t);
     return t * kTile + (it % (kTile / kBN)) * kBN;
@@ -266,6 +271,48 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) S[qb][kb][r] = -INFINITY;
         }
+  };
+  // Frame window (kMode 2): a key frame is allowed for this lane's query frame
+  // if their chunks are within wp.neighbours of each other or either frame is
+  // the first or last one.  frame_tokens >= 64, so a 64-key stage spans at
+  // most two frames; stages where every lane allows both skip the masking.
+  // Frame 0 is an anchor and every list starts with key tile 0, so stage 0
+  // (keys 0..63, all of frame 0) is open to every row: the running max is
+  // finite from the prologue on, and a later stage masked whole for a row adds
+  // exp2(-inf) = 0 to it.
+  int q_chunk[kQB];
+  bool q_anchor[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qf = kMode == 2 ? (q0 + 32 * qb + l32) / wp.frame_tokens : 0;
+    q_chunk[qb] = kMode == 2 ? qf / wp.chunk_frames : 0;
+    q_anchor[qb] = qf == 0 || qf >= wp.frames - 1;
+  }
+  auto frame_ok = [&](int qb, int kf) {
+    const int dc = q_chunk[qb] - kf / wp.chunk_frames;
+    return q_anchor[qb] || kf == 0 || kf == wp.frames - 1 || (dc <= wp.neighbours && -dc <= wp.neighbours);
+  };
+  auto window_mask = [&](f32x16 (&S)[kQB][kKB], int kv0) {
+    const int kf0 = kv0 / wp.frame_tokens;
+    const int next_frame = (kf0 + 1) * wp.frame_tokens;   // first key of frame kf0 + 1
+    bool ok0[kQB], ok1[kQB];
+    bool need = kv0 + kBN > N;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      ok0[qb] = frame_ok(qb, kf0);
+      ok1[qb] = next_frame >= kv0 + kBN || frame_ok(qb, kf0 + 1);
+      need = need || !ok0[qb] || !ok1[qb];
+    }
+    if (!__builtin_amdgcn_ballot_w64(need)) return;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * kb + 16 * g + r;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          if (key >= N || !(key < next_frame ? ok0[qb] : ok1[qb])) S[qb][kb][r] = -INFINITY;
+      }
   };
   // Row max of a stage, in scaled log2 units.
   auto rowmax = [&](const f32x16 (&S)[kQB][kKB], float (&mx)[kQB]) {
@@ -390,7 +437,11 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       }
     }
 
-    if (has_next && kv_next + kBN > N) mask(Snext, kv_next);
+    if constexpr (kMode == 2) {
+      if (has_next) window_mask(Snext, kv_next);
+    } else if (has_next && kv_next + kBN > N) {
+      mask(Snext, kv_next);
+    }
 
     float mx[kQB];
     // Raise this wave's issue priority for the MFMA-heavy PV region: when the
@@ -429,7 +480,8 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     __builtin_amdgcn_s_waitcnt(kWaitVm(0));
     __builtin_amdgcn_s_barrier();
     qk(Buf<0>(), SA);
-    if (kv0 + kBN > N) mask(SA, kv0);
+    if constexpr (kMode == 2) window_mask(SA, kv0);
+    else if (kv0 + kBN > N) mask(SA, kv0);
     float mx[kQB];
     rowmax(SA, mx);
     maybe_rescale(mx);
@@ -473,12 +525,13 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 
 // kQB = 1: 32 query rows per wave, two waves per SIMD (256 registers each);
 // kQB = 2: 64 rows per wave, one wave per SIMD with the whole register file.
-template <bool kSparse, int kWaves, int kStages, int kQB, int kBN>
+template <int kMode, int kWaves, int kStages, int kQB, int kBN>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3 - kQB, 3 - kQB))) void
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                const int32_t* __restrict__ idx, int keep, int N, int qtiles, float c) {
-  attn_fwd_body<kSparse, kWaves, kStages, kQB, kBN>(Q, K, V, O, idx, keep, N, qtiles, c);
+                const int32_t* __restrict__ idx, int keep, int N, int qtiles, float c,
+                WindowParams wp) {
+  attn_fwd_body<kMode, kWaves, kStages, kQB, kBN>(Q, K, V, O, idx, keep, N, qtiles, c, wp);
 }
 
 }  // namespace
@@ -492,17 +545,29 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     const int qtiles = (tokens + kTile - 1) / kTile;
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
-    attn_fwd_kernel<true, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        q, k, v, out, idx, keep, tokens, qtiles, c);
+    attn_fwd_kernel<1, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        q, k, v, out, idx, keep, tokens, qtiles, c, WindowParams{});
   } else {
     // 256 query rows per workgroup (8 waves) share each K/V stage; one
     // workgroup per CU leaves LDS for three slots, loads two stages ahead
     const int qtiles = (tokens + 255) / 256;
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
-    attn_fwd_kernel<false, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
-        q, k, v, out, idx, keep, tokens, qtiles, c);
+    attn_fwd_kernel<0, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+        q, k, v, out, idx, keep, tokens, qtiles, c, WindowParams{});
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* idx, const WindowParams& wp,
+                                   int heads, int tokens, float scale, hipStream_t stream) {
+  const float c = scale * 1.4426950408889634f;  // scale * log2(e)
+  const int qtiles = (tokens + kTile - 1) / kTile;
+  const long long blocks = (long long)heads * qtiles;
+  if (blocks <= 0) return hipSuccess;
+  attn_fwd_kernel<2, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      q, k, v, out, idx, 0, tokens, qtiles, c, wp);
   return hipGetLastError();
 }
 

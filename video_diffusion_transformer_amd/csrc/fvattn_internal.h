@@ -10,11 +10,33 @@ namespace fvattn {
 constexpr int kHeadDim = 128;
 constexpr int kTile = 128;        // selection tile (tokens)
 
+// Frame-window description for the windowed softmax (latent frames of
+// frame_tokens tokens, chunks of chunk_frames frames, `neighbours` chunks on
+// each side, first and last frame as anchors); counts[t] = number of key tiles
+// listed for query tile t.
+struct WindowParams {
+  const int32_t* counts = nullptr;
+  int frame_tokens = 0;
+  int chunk_frames = 1;
+  int neighbours = 0;
+  int frames = 0;
+};
+
 // Dense (idx == nullptr) or tile-list (idx != nullptr, `keep` entries per query
 // tile) attention forward over `heads` heads.
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             uint16_t* out, const int32_t* idx, int keep, int heads, int tokens,
                             float scale, hipStream_t stream);
+
+// Windowed softmax: key-tile lists idx [T][T] (row t lists counts[t] tiles,
+// ascending; shared by every head).
+hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   uint16_t* out, const int32_t* idx, const WindowParams& wp,
+                                   int heads, int tokens, float scale, hipStream_t stream);
+
+// Key-tile lists of the frame window: idx [T][T] (padded with -1), counts [T].
+hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int32_t* idx, int32_t* counts,
+                               hipStream_t stream);
 
 // S1: fp64 tile means.  transposed == false: out [heads][T][128];
 // transposed == true: out [heads][128][T].
