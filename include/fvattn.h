@@ -138,7 +138,8 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
  * frames with 1 neighbour on each side give the page's 15-frame window).
  * q, k, v, out as in fvattn_forward.  frame_tokens >= 64 (else
  * FVATTN_ERR_UNSUPPORTED), chunk_frames >= 1, neighbours >= 0.  Uses
- * stream-ordered scratch for the key-tile lists (T*T + T int32). */
+ * stream-ordered scratch for the key-tile lists (ceil(tokens/256) * (T + 1)
+ * int32). */
 int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
                           int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,
                           int neighbours, void* stream);

@@ -244,7 +244,8 @@ int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neig
   wp.chunk_frames = chunk_frames;
   wp.neighbours = neighbours;
   wp.frames = (tokens - 1) / frame_tokens + 1;
-  return hip_status(fvattn::launch_window_tiles(tokens, wp, idx_out, count_out, (hipStream_t)stream));
+  return hip_status(
+      fvattn::launch_window_tiles(tokens, wp, kTile, false, idx_out, count_out, (hipStream_t)stream));
 }
 
 int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
@@ -262,9 +263,11 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   if (rc != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const int T = tiles_of(tokens);
+  const int blocks = (tokens - 1) / fvattn::kWindowRows + 1;
   void* scratch = nullptr;
-  const size_t idx_bytes = align256(sizeof(int32_t) * (size_t)T * T);
-  if (hipMallocAsync(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)T), st) != hipSuccess) {
+  const size_t idx_bytes = align256(sizeof(int32_t) * (size_t)blocks * T);
+  if (hipMallocAsync(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)blocks), st) !=
+      hipSuccess) {
     (void)hipGetLastError();
     return FVATTN_ERR_ALLOC;
   }
@@ -276,7 +279,8 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   wp.chunk_frames = chunk_frames;
   wp.neighbours = neighbours;
   wp.frames = (tokens - 1) / frame_tokens + 1;
-  hipError_t e = fvattn::launch_window_tiles(tokens, wp, idx, counts, st);
+  wp.first_block = (int)((long long)(wp.frames - 1) * frame_tokens / fvattn::kWindowRows);
+  hipError_t e = fvattn::launch_window_tiles(tokens, wp, fvattn::kWindowRows, true, idx, counts, st);
   if (e == hipSuccess)
     e = fvattn::launch_attention_window((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                         (uint16_t*)out, idx, wp, heads, tokens, scale, st);

@@ -1,44 +1,47 @@
-// Fused attention forward for gfx950 (MI355X): dense, or restricted to a list
-// of 128-token key tiles per 128-token query tile (block-sparse).
+// Fused attention forward for gfx950 (MI355X): dense, restricted to a list of
+// 128-token key tiles per 128-token query tile (block-sparse), or restricted
+// to a frame window (Video DeltaNet's softmax branch).
 //
 // What it computes: out = softmax(scale * Q K^T) V per head, non-causal, the
-// softmax taken over every key (dense) or over the keys of the listed tiles
-// only (sparse); the scores are streamed tile by tile with an online softmax
-// and never stored (FreeVideo page, section "Why it does not fit: the
-// arithmetic"; FastH3 page, section "Lever two: VSA-H3 makes each of the four
-// calls cheaper", fine stage: exact attention over the surviving tiles).
+// softmax taken over every key (dense), over the keys of the listed tiles only
+// (sparse), or over the keys of the allowed frames (window); the scores are
+// streamed tile by tile with an online softmax and never stored (FreeVideo
+// page, section "Why it does not fit: the arithmetic"; FastH3 page, section
+// "Lever two: VSA-H3 makes each of the four calls cheaper", fine stage: exact
+// attention over the surviving tiles; FreeVideo page, section "Where Video
+// DeltaNet comes in", for the window).
 //
-// Design (one workgroup = one head x one 128-row query tile; 2 waves of 64
-// query rows; 2 workgroups per CU, so one wave per SIMD with the whole
-// 512-entry register file):
+// Design (one workgroup = one head x kBM query rows, one wave per 32 rows;
+// dense and window: 8 waves, 256 rows, one workgroup per CU; sparse: 4 waves,
+// 128 rows = one selection tile, two workgroups per CU; either way two waves
+// per SIMD with 256 registers each):
 // * Both products run on the bf16 matrix cores, v_mfma_f32_32x32x16_bf16, in
 //   transposed form: S^T = K Q^T (A = K from LDS, B = Q^T held in registers for
 //   the whole kernel) and O^T = V^T P^T (A = V^T from LDS, B = P^T taken
 //   straight from the S^T accumulators).  With this orientation every lane owns
 //   one query column of S^T and of O^T, so the softmax max/sum and the O
 //   rescale are per-lane scalars plus one swap between the two half-waves
-//   (v_permlane32_swap, no LDS traffic).  Each wave covers two 32-row query
-//   blocks, so every K or V operand read from LDS feeds two MFMAs.
+//   (v_permlane32_swap, no LDS traffic).
 // * The key rows fed to the S^T product are permuted inside each 32-key block
 //   so that half-wave g ends up holding keys 16g..16g+15 contiguously; P^T can
 //   then be passed to the PV product without any data movement.
-// * K and V stream through LDS in 32-key stages, double buffered, written by
-//   the buffer-load-to-LDS path (no registers involved).  The buffer
-//   descriptor of each stage starts at the stage's first key and ends at the
-//   last token, so the hardware range check zero-fills rows past the sequence
-//   end.  K and V are stored row-major with XOR swizzles on 16-byte chunks (each
-//   lane fetches the global chunk that belongs at its LDS slot).  The V^T
-//   operand is read with the gfx950 LDS transpose load ds_read_b64_tr_b16.
-// * Software pipeline per 32-key stage j: the S^T MFMAs of stage j+1 run while
-//   the softmax of stage j (exp2, row sums, bf16 packing) runs on the vector
-//   ALU; then the PV MFMAs of stage j run while the row max of stage j+1 is
-//   taken.  The interleaving is pinned with scheduling group barriers.  The
-//   scores alternate between two register sets across the two unrolled stages,
-//   so the softmax of one stage and the S^T product of the next never touch
-//   the same registers.  One barrier per stage; the loads of K(j+2) and V(j+1)
-//   are in flight for the whole stage.  The wave raises its issue priority for
-//   the PV region, so a SIMD shared with a wave in its softmax keeps the matrix
-//   pipe busy.
+// * K and V stream through LDS in 64-key stages, two slots each, written by the
+//   buffer-load-to-LDS path (no registers involved); K runs two stages ahead
+//   and V one.  The buffer descriptor of each stage starts at the stage's first
+//   key and ends at the last token, so the hardware range check zero-fills rows
+//   past the sequence end.  K and V are stored row-major with XOR swizzles on
+//   16-byte chunks (each lane fetches the global chunk that belongs at its LDS
+//   slot); the V^T operand is read with the gfx950 LDS transpose load
+//   ds_read_b64_tr_b16.  Each slot is its own LDS array and the stage waits
+//   are explicit vmcnt counts before a bare barrier, so no LDS read waits for
+//   loads it does not consume.
+// * Software pipeline per stage j: the S^T MFMAs of stage j+1 run while the
+//   softmax of stage j (exp2, row sums, bf16 packing) runs on the vector ALU;
+//   then the PV MFMAs of stage j run while the row max of stage j+1 is taken.
+//   The interleaving is pinned with scheduling group barriers.  The scores
+//   alternate between two register sets across two unrolled stages.  The wave
+//   raises its issue priority for the PV region, so a SIMD shared with a wave
+//   in its softmax keeps the matrix pipe busy.
 // * fp32 online softmax in the exp2 domain (scale * log2 e folded into one
 //   FMA per score).  The running max is only raised, and O and the running sum
 //   rescaled, when some row of the wave sees a score more than 2^8 above it
@@ -46,7 +49,7 @@
 //   exactly as well as they hold 1.  P is rounded to bf16 for the PV product,
 //   out to bf16.
 // * Workgroups are remapped so each of the 8 XCDs walks a contiguous range of
-//   (head, query tile) pairs, keeping one head's K/V hot in that XCD's L2.
+//   (head, query block) pairs, keeping one head's K/V hot in that XCD's L2.
 
 #include <math.h>
 
@@ -133,7 +136,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   constexpr int kBM = 32 * kQB * kWaves;
   constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
   constexpr int kPrefetch = kStages - 1;
-  static_assert(kMode == 0 || kBM == kTile, "tile-list workgroups cover one selection tile");
+  static_assert(kMode != 1 || kBM == kTile, "per-head lists cover one selection tile");
   // One LDS array per slot: distinct objects let the compiler see that a read
   // of one slot cannot alias a buffer-to-LDS load still landing in another,
   // so it does not wait for every load in flight before each LDS read.
@@ -145,7 +148,9 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   unsigned char* const v_slots[3] = {v_lds0, v_lds1, v_lds2};
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = L / qtiles, qt = L - h * qtiles;
+  const int h = L / qtiles, qs = L - h * qtiles;
+  const int qt = kMode != 2 ? qs : (qs + wp.first_block < qtiles ? qs + wp.first_block
+                                                                 : qs + wp.first_block - qtiles);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
@@ -170,17 +175,36 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       }
   }
 
+  const int ktiles = (N + kTile - 1) / kTile;
   const int32_t* irow = kMode == 1   ? idx + ((size_t)h * qtiles + qt) * keep
-                        : kMode == 2 ? idx + (size_t)qt * qtiles
+                        : kMode == 2 ? idx + (size_t)qt * ktiles
                                      : nullptr;
   const int nsub = kMode == 0 ? (N + kBN - 1) / kBN
                               : (kTile / kBN) * (kMode == 1 ? keep : wp.counts[qt]);
-  auto kv_start = [&](int it) -> int {
-    if (kMode == 0) return it * kBN;
-    int t = irow[it / (kTile / kBN)];
-    t = t < 0 ? 0 : (t >= qtiles ? qtiles - 1 : t);
-    return t * kTile + (it % (kTile / kBN)) * kBN;
+  // List entry of stage i (any i >= 0: past the end it repeats the last
+  // entry, so the load never leaves the list), and the first key of stage i
+  // from its entry.  Window lists flag (kMaskFlag) the key tiles that need
+  // per-element masking for some row of this block; kv_of passes the flag on.
+  constexpr int kSub = kTile / kBN;   // stages per key tile
+  const int nlist = kMode == 1 ? keep : kMode == 2 ? wp.counts[qt] : 1;
+  auto entry = [&](int i) -> int {
+    const int j = i / kSub;
+    return irow[j < nlist ? j : nlist - 1];
   };
+  auto kv_of = [&](int e, int i) -> int {
+    if (kMode == 0) return i * kBN;
+    const int flag = kMode == 2 ? (e & kMaskFlag) : 0;
+    int t = kMode == 2 ? (e & ~kMaskFlag) : e;
+    t = t < 0 ? 0 : (t >= ktiles ? ktiles - 1 : t);
+    return (t * kTile + (i % kSub) * kBN) | flag;
+  };
+  auto kv_start = [&](int i) -> int { return kv_of(kMode == 0 ? 0 : entry(i), i); };
+  // Raw entries of stages it+1 .. it+kStages, loaded one stage before use and
+  // decoded only where used, so no stage waits on a scalar list load it has
+  // just issued.
+  int ring[kStages];
+#pragma unroll
+  for (int j = 0; j < kStages; ++j) ring[j] = kMode != 0 ? entry(1 + j) : 0;
 
   // Buffer-to-LDS loads: wave-wide load i of this wave fills LDS rows
   // 4 (kLoadsPerWave wave + i) + (lane >> 4), 16-byte slot lane & 15; the lane
@@ -414,9 +438,12 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     // consumed), so no wave can still be reading the slots refilled below.
     __builtin_amdgcn_s_barrier();
     const bool has_next = it + 1 < nsub;
-    const int kv_next = has_next ? kv_start(it + 1) : 0;
-    if (it + kStages < nsub) load_k(kv_start(it + kStages), Buf<k % kStages>());
-    if (it + kPrefetch < nsub) load_v(kv_start(it + kPrefetch), Buf<(k + kStages - 1) % kStages>());
+    // dense stages are plain arithmetic; list stages come from the ring
+    const int kv_next = kv_of(ring[0], it + 1);
+    if (it + kStages < nsub) load_k(kv_of(ring[kStages - 1], it + kStages) & ~kMaskFlag, Buf<k % kStages>());
+    if (it + kPrefetch < nsub)
+      load_v(kv_of(ring[kPrefetch - 1], it + kPrefetch) & ~kMaskFlag, Buf<(k + kStages - 1) % kStages>());
+    const int ahead = kMode != 0 ? entry(it + 1 + kStages) : 0;
 
     softmax(Scur, P);
     qk(Buf<kSlotK>(), Snext);
@@ -438,7 +465,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     }
 
     if constexpr (kMode == 2) {
-      if (has_next) window_mask(Snext, kv_next);
+      if (has_next && (kv_next & kMaskFlag)) window_mask(Snext, kv_next & ~kMaskFlag);
     } else if (has_next && kv_next + kBN > N) {
       mask(Snext, kv_next);
     }
@@ -467,20 +494,28 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 
     __builtin_amdgcn_s_setprio(0);
     if (has_next) maybe_rescale(mx);
+    if constexpr (kMode != 0) {
+#pragma unroll
+      for (int j = 0; j + 1 < kStages; ++j) ring[j] = ring[j + 1];
+      ring[kStages - 1] = ahead;
+    }
   };
 
   // prologue: K(0..kStages-1) and V(0..kStages-2) started, scores and max of stage 0
   {
-    const int kv0 = kv_start(0);
+    const int kv0e = kv_start(0), kv0 = kv0e & ~kMaskFlag;
     load_k(kv0, Buf<0>());
-    if (1 < nsub) load_k(kv_start(1), Buf<1 % kStages>());
-    if (kStages > 2 && 2 < nsub) load_k(kv_start(2), Buf<2 % kStages>());
+    const int kv1 = kv_of(ring[0], 1) & ~kMaskFlag;
+    if (1 < nsub) load_k(kv1, Buf<1 % kStages>());
+    if (kStages > 2 && 2 < nsub) load_k(kv_of(ring[1], 2) & ~kMaskFlag, Buf<2 % kStages>());
     load_v(kv0, Buf<0>());
-    if (kStages > 2 && 1 < nsub) load_v(kv_start(1), Buf<1 % kStages>());
+    if (kStages > 2 && 1 < nsub) load_v(kv1, Buf<1 % kStages>());
     __builtin_amdgcn_s_waitcnt(kWaitVm(0));
     __builtin_amdgcn_s_barrier();
     qk(Buf<0>(), SA);
-    if constexpr (kMode == 2) window_mask(SA, kv0);
+    if constexpr (kMode == 2) {
+      if (kv0e & kMaskFlag) window_mask(SA, kv0);
+    }
     else if (kv0 + kBN > N) mask(SA, kv0);
     float mx[kQB];
     rowmax(SA, mx);
@@ -562,11 +597,13 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
 hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    uint16_t* out, const int32_t* idx, const WindowParams& wp,
                                    int heads, int tokens, float scale, hipStream_t stream) {
+  // the dense shape: 256 query rows per workgroup (8 waves); idx and
+  // wp.counts hold one list per 256-row block (kWindowRows)
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  const int qtiles = (tokens + kTile - 1) / kTile;
+  const int qtiles = (tokens + kWindowRows - 1) / kWindowRows;
   const long long blocks = (long long)heads * qtiles;
   if (blocks <= 0) return hipSuccess;
-  attn_fwd_kernel<2, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+  attn_fwd_kernel<2, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
       q, k, v, out, idx, 0, tokens, qtiles, c, wp);
   return hipGetLastError();
 }

@@ -20,6 +20,10 @@ struct WindowParams {
   int chunk_frames = 1;
   int neighbours = 0;
   int frames = 0;
+  // query block walked first within each head: the blocks from here to the
+  // end (they hold the last frame, whose rows see every key) are the longest,
+  // and starting with them keeps them out of the tail of the launch
+  int first_block = 0;
 };
 
 // Dense (idx == nullptr) or tile-list (idx != nullptr, `keep` entries per query
@@ -28,15 +32,24 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             uint16_t* out, const int32_t* idx, int keep, int heads, int tokens,
                             float scale, hipStream_t stream);
 
-// Windowed softmax: key-tile lists idx [T][T] (row t lists counts[t] tiles,
-// ascending; shared by every head).
+// Query rows per workgroup of the windowed softmax, and so per key-tile list.
+constexpr int kWindowRows = 256;
+// Bit set in an internal window-list entry when the key tile needs
+// per-element masking for some row of the block (a disallowed frame, or keys
+// past the sequence end).
+constexpr int kMaskFlag = 1 << 30;
+
+// Windowed softmax: key-tile lists idx [ceil(N / kWindowRows)][T] (row b lists
+// counts[b] tiles, ascending; shared by every head).
 hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    uint16_t* out, const int32_t* idx, const WindowParams& wp,
                                    int heads, int tokens, float scale, hipStream_t stream);
 
-// Key-tile lists of the frame window: idx [T][T] (padded with -1), counts [T].
-hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int32_t* idx, int32_t* counts,
-                               hipStream_t stream);
+// Key-tile lists of the frame window for query blocks of q_rows rows (a
+// multiple of 128): idx [ceil(N / q_rows)][T] (padded with -1), counts
+// [ceil(N / q_rows)]; with `flags`, entries carry kMaskFlag.
+hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int q_rows, bool flags,
+                               int32_t* idx, int32_t* counts, hipStream_t stream);
 
 // S1: fp64 tile means.  transposed == false: out [heads][T][128];
 // transposed == true: out [heads][128][T].

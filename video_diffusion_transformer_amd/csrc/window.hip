@@ -3,43 +3,58 @@
 // of latent frames sees its neighbouring chunks, and the first and last
 // frames see and are seen by every frame).
 //
-// One wave per 128-token query tile.  A key tile is listed when some query of
-// the tile may attend to some key of it.  Frames inside a tile are contiguous
+// One wave per block of q_rows query tokens (128 for the public lists, 256 for
+// the attention workgroups).  A key tile is listed when some query of the
+// block may attend to some key of it.  Frames inside a tile are contiguous
 // and chunks grow with frames, so this is a closed-form interval test: either
 // tile holds an anchor frame, or the chunk ranges of the two tiles lie within
 // `neighbours` of each other.  Listed tiles are compacted in ascending order
 // with ballots; the rest of the row is filled with -1.
+//
+// For the attention kernel a listed tile is also flagged when some pair of a
+// query of the block and a key of the tile is disallowed (or the tile is cut
+// by the sequence end), so that only flagged tiles pay for per-element
+// masking.  Every pair is allowed when one side's non-anchor frames are empty
+// or the farthest pair of non-anchor chunks is within `neighbours`.
 
 #include "fvattn_internal.h"
 
 namespace fvattn {
 namespace {
 
-__global__ __launch_bounds__(64) void window_tiles_kernel(int N, WindowParams wp, int T,
+__global__ __launch_bounds__(64) void window_tiles_kernel(int N, WindowParams wp, int q_rows,
+                                                          bool flags, int T,
                                                           int32_t* __restrict__ idx,
                                                           int32_t* __restrict__ counts) {
   const int t = blockIdx.x, lane = threadIdx.x;
   const int ft = wp.frame_tokens, chunk = wp.chunk_frames, nb = wp.neighbours;
   const int last = wp.frames - 1;
-  const int q_lo = t * kTile, q_hi = (q_lo + kTile < N ? q_lo + kTile : N) - 1;
+  const int q_lo = t * q_rows, q_hi = (q_lo + q_rows < N ? q_lo + q_rows : N) - 1;
   const int qf_lo = q_lo / ft, qf_hi = q_hi / ft;
   const bool q_anchor = qf_lo == 0 || qf_hi >= last;
   const int qc_lo = qf_lo / chunk, qc_hi = qf_hi / chunk;
+  // non-anchor query frames [qa_lo, qa_hi] (empty when qa_lo > qa_hi)
+  const int qa_lo = qf_lo > 1 ? qf_lo : 1, qa_hi = qf_hi < last - 1 ? qf_hi : last - 1;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* row = idx + (size_t)t * T;
   int base = 0;
   for (int j0 = 0; j0 < T; j0 += 64) {
     const int j = j0 + lane;
     bool need = false;
+    int entry = j;
     if (j < T) {
       const int k_lo = j * kTile, k_hi = (k_lo + kTile < N ? k_lo + kTile : N) - 1;
       const int kf_lo = k_lo / ft, kf_hi = k_hi / ft;
       const bool k_anchor = kf_lo == 0 || kf_hi >= last;
       const int kc_lo = kf_lo / chunk, kc_hi = kf_hi / chunk;
       need = q_anchor || k_anchor || (kc_lo <= qc_hi + nb && kc_hi >= qc_lo - nb);
+      const int ka_lo = kf_lo > 1 ? kf_lo : 1, ka_hi = kf_hi < last - 1 ? kf_hi : last - 1;
+      const bool all_ok = qa_lo > qa_hi || ka_lo > ka_hi ||
+                          (ka_hi / chunk - qa_lo / chunk <= nb && qa_hi / chunk - ka_lo / chunk <= nb);
+      if (flags && (!all_ok || k_hi - k_lo + 1 < kTile)) entry |= kMaskFlag;
     }
     const uint64_t m = __ballot(need);
-    if (need) row[base + __popcll(m & lt)] = j;
+    if (need) row[base + __popcll(m & lt)] = entry;
     base += __popcll(m);
   }
   for (int p = base + lane; p < T; p += 64) row[p] = -1;
@@ -48,11 +63,13 @@ __global__ __launch_bounds__(64) void window_tiles_kernel(int N, WindowParams wp
 
 }  // namespace
 
-hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int32_t* idx, int32_t* counts,
-                               hipStream_t stream) {
+hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int q_rows, bool flags,
+                               int32_t* idx, int32_t* counts, hipStream_t stream) {
   const int T = (tokens + kTile - 1) / kTile;
+  const int blocks = (tokens + q_rows - 1) / q_rows;
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(window_tiles_kernel, dim3(T), dim3(64), 0, stream, tokens, wp, T, idx, counts);
+  hipLaunchKernelGGL(window_tiles_kernel, dim3(blocks), dim3(64), 0, stream, tokens, wp, q_rows,
+                     flags, T, idx, counts);
   return hipGetLastError();
 }
 
