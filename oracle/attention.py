@@ -88,9 +88,9 @@ def dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, rows=None,
 # coarse pooled scores first, then compute_topk decides how many survive)
 # --------------------------------------------------------------------------
 
-def tile_count(tokens: int) -> int:
-    """Number of contiguous 128-token tiles covering ``tokens`` tokens."""
-    return -(-tokens // TILE)
+def tile_count(tokens: int, tile: int = TILE) -> int:
+    """Number of contiguous ``tile``-token tiles (128 by default) covering ``tokens`` tokens."""
+    return -(-tokens // tile)
 
 
 def keep_count(num_tiles: int, keep_frac: float) -> int:
@@ -103,7 +103,7 @@ def keep_count(num_tiles: int, keep_frac: float) -> int:
     return max(1, min(math.ceil(keep_frac * num_tiles), num_tiles))
 
 
-def tile_means(x: np.ndarray) -> np.ndarray:
+def tile_means(x: np.ndarray, tile: int = TILE) -> np.ndarray:
     """Mean of each tile's valid tokens, for one head.
 
     x: [N, d] float64.  Returns [T, d] float64.  Each tile sum runs in token
@@ -111,11 +111,11 @@ def tile_means(x: np.ndarray) -> np.ndarray:
     number of valid tokens in the tile.
     """
     N, d = x.shape
-    T = tile_count(N)
-    starts = np.arange(T) * TILE
-    counts = np.minimum(starts + TILE, N) - starts
+    T = tile_count(N, tile)
+    starts = np.arange(T) * tile
+    counts = np.minimum(starts + tile, N) - starts
     acc = np.zeros((T, d), dtype=np.float64)
-    for i in range(TILE):          # i-th token of every tile, in token order
+    for i in range(tile):          # i-th token of every tile, in token order
         live = i < counts
         acc[live] = acc[live] + x[starts[live] + i]
     return acc / counts[:, None].astype(np.float64)
@@ -148,17 +148,17 @@ def top_tiles(sigma: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
-def select_tiles(q: np.ndarray, k: np.ndarray, keep_frac: float) -> np.ndarray:
+def select_tiles(q: np.ndarray, k: np.ndarray, keep_frac: float, tile: int = TILE) -> np.ndarray:
     """Tile indices kept for every head and query tile.
 
     q, k: [H, N, d] float64.  Returns int32 [H, T, kk] with kk = keep_count(T, keep_frac).
     """
     H, N, _ = q.shape
-    T = tile_count(N)
+    T = tile_count(N, tile)
     kk = keep_count(T, keep_frac)
     out = np.empty((H, T, kk), dtype=np.int32)
     for h in range(H):
-        sigma = tile_scores(tile_means(q[h]), tile_means(k[h]))
+        sigma = tile_scores(tile_means(q[h], tile), tile_means(k[h], tile))
         out[h] = top_tiles(sigma, kk)
     return out
 
@@ -167,13 +167,13 @@ def select_tiles(q: np.ndarray, k: np.ndarray, keep_frac: float) -> np.ndarray:
 # sparse attention (exact attention over the kept tiles only)
 # --------------------------------------------------------------------------
 
-def kept_keys(tiles, tokens: int) -> np.ndarray:
+def kept_keys(tiles, tokens: int, tile: int = TILE) -> np.ndarray:
     """Token indices of the given tiles (valid tokens only), tile order kept."""
-    return np.concatenate([np.arange(t * TILE, min(t * TILE + TILE, tokens)) for t in tiles])
+    return np.concatenate([np.arange(t * tile, min(t * tile + tile, tokens)) for t in tiles])
 
 
 def sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, idx: np.ndarray,
-           rows=None) -> np.ndarray:
+           rows=None, tile: int = TILE) -> np.ndarray:
     """Block-sparse attention: query i of tile t sees only the tokens of tiles idx[h, t].
 
     q, k, v: [H, N, d] float64; idx: int [H, T, kk].  ``rows`` as in ``dense``.
@@ -181,11 +181,11 @@ def sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, idx: np.nd
     H, N, d = q.shape
     rows = np.arange(N) if rows is None else np.asarray(rows)
     out = np.empty((H, len(rows), d), dtype=np.float64)
-    tile_of = rows // TILE
+    tile_of = rows // tile
     for h in range(H):
         for t in np.unique(tile_of):
             sel = np.nonzero(tile_of == t)[0]
-            keys = kept_keys(idx[h, t], N)
+            keys = kept_keys(idx[h, t], N, tile)
             out[h, sel] = attention_rows(q[h, rows[sel]], k[h, keys], v[h, keys], scale)
     return out
 
