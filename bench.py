@@ -70,6 +70,22 @@ def window_flops(tokens: int, frame_tokens: int, chunk: int, nb: int, heads: int
     return 4.0 * d * heads * pairs
 
 
+def vsa_flops(idx, prefix: int, grid, tile, d: int = 128) -> float:
+    """QK^T + PV FLOPs of VSA-H3 attention: non-video rows see every key; a
+    video query tile sees the prefix plus the tokens of its kept tiles."""
+    import numpy as np
+    frames, height, width = grid
+    tt, th, tw = tile
+    sizes = np.array([min(tt, frames - a) * min(th, height - b) * min(tw, width - c)
+                      for a in range(0, frames, tt) for b in range(0, height, th)
+                      for c in range(0, width, tw)], dtype=np.float64)
+    n = prefix + frames * height * width
+    pairs = prefix * float(n) * idx.shape[0]
+    kept = sizes[idx].sum(axis=2)                       # [H, Tv] kept video keys
+    pairs += float((sizes[None, :] * (prefix + kept)).sum())
+    return 4.0 * d * pairs
+
+
 def cpu_baseline(q, k, v, scale, budget_s: float):
     """The fp64 oracle on head 0 of the same workload: full selection, then dense and
     sparse attention for consecutive query tiles until the time budget is spent."""
@@ -114,9 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse", "window"], default=None,
+    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa"], default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
-                         "0 for window, which is timed outside the step)")
+                         "0 for window and vsa, which are timed outside the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration runs)")
     args = ap.parse_args()
@@ -166,6 +182,7 @@ def main():
     do_dense = args.only in (None, "dense")
     do_sparse = args.only in (None, "sparse")
     do_window = args.only in (None, "window")
+    do_vsa = args.only in (None, "vsa")
     if not do_dense:
         flop_dense = 0.0
     if not do_sparse:
@@ -242,6 +259,36 @@ def main():
                   "tflops_visited": round(flop_w_visited / (wm * 1e-3) / 1e12, 2),
                   "density": round(flop_w / (4.0 * TOKENS * TOKENS * 128 * HEADS), 4)}
 
+    # VSA-H3 packed sequence, outside the step: a 512-token non-video prefix
+    # ahead of the same 72 x 24 x 42 video grid, (4, 4, 4) tiles, 90% sparse,
+    # all 56 heads in one call (new inputs: the prefix shifts the video tokens)
+    vsa = None
+    if do_vsa:
+        del qd, kd, vd, out_dense, out_sparse
+        torch.cuda.empty_cache()
+        prefix, grid, tile = inputs.VSA_PREFIX, inputs.VSA_GRID_72, (4, 4, 4)
+        log("generating VSA inputs", prefix, "+", grid)
+        pq, pk, pv = (t.to(dev) for t in inputs.make_packed_qkv(prefix, grid, HEADS, SEED))
+        pout = torch.empty_like(pq)
+        v_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        v_ms = []
+        for i in range(4):
+            v_ev[0].record(stream)
+            fv.forward_vsa(pq, pk, pv, prefix, grid, tile, KEEP_FRAC, scale=scale, out=pout)
+            v_ev[1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                v_ms.append(v_ev[0].elapsed_time(v_ev[1]))
+        vidx = fv.vsa_select(pq, pk, prefix, grid, tile, KEEP_FRAC).cpu().numpy()
+        del pq, pk, pv, pout
+        vm = float(np.median(v_ms))
+        flop_v = vsa_flops(vidx, prefix, grid, tile)
+        ntok = prefix + grid[0] * grid[1] * grid[2]
+        vsa = {"ms": round(vm, 3), "flop": flop_v, "prefix": prefix, "grid": list(grid),
+               "tile": list(tile), "keep_tiles": int(vidx.shape[2]), "video_tiles": int(vidx.shape[1]),
+               "tflops_effective": round(flop_v / (vm * 1e-3) / 1e12, 2),
+               "density": round(flop_v / (4.0 * ntok * ntok * 128 * HEADS), 4)}
+
     d_ms = float(np.median(dense_ms))
     s_ms = float(np.median(sparse_ms))
     dense_tflops = flop_dense / max(d_ms * 1e-3, 1e-12) / 1e12
@@ -294,6 +341,8 @@ def main():
         if do_dense:
             window["speedup_vs_dense"] = round(d_ms / window["ms"], 3)
         result["window"] = window
+    if vsa is not None:
+        result["vsa"] = vsa
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), budget", args.cpu_budget, "s")
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)

@@ -39,8 +39,9 @@
  *   sub-array.  Index arrays are int32 [heads][T][k], T = ceil(tokens/128),
  *   device pointers, ascending within each row.
  * Ownership: the caller owns every buffer and the stream.  The library never
- *   frees caller memory.  Sparse mode allocates its scratch (tile means and
- *   index lists) stream-ordered on the caller's stream and releases it there.
+ *   frees caller memory.  Sparse mode allocates its scratch (tile means, the
+ *   fp64 tile score matrix [heads][T][T] and index lists) stream-ordered on
+ *   the caller's stream and releases it there.
  * Stream: `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call only enqueues work and returns; no host
  *   synchronization happens inside.
@@ -150,6 +151,45 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
  * count_out[t] indices followed by -1; count_out: int32 [T] device. */
 int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neighbours,
                         int32_t* idx_out, int32_t* count_out, void* stream);
+
+/* VSA-H3 packed-sequence attention (FastH3 page, section "Lever two: VSA-H3
+ * makes each of the four calls cheaper").  The sequence is packed as
+ * [prefix_tokens non-video tokens (text, condition keyframes, audio) |
+ * generated video], the video part a frames x height x width latent grid in
+ * (t, h, w) raster order (24 x 42 per latent frame at 1344x768), so tokens =
+ * prefix_tokens + frames * height * width.  The video part is cut into
+ * tile_t x tile_h x tile_w tiles over that grid ((4, 4, 4) = 64 tokens, the
+ * shape FastH3 is trained on, or (4, 8, 8) = 256; the tile size must be 64,
+ * 128 or 256), enumerated t-tile slowest, w-tile fastest; tiles at a grid
+ * edge the tile does not divide are partial.  Each video query tile keeps the
+ * k = max(1, min(ceil(keep_frac * Tv), Tv)) video key tiles of highest pooled
+ * score (Tv = number of video tiles; means over each tile's valid tokens,
+ * summed in (t, h, w) order; scores, ties and order as in the selection rule
+ * above).  A video query attends to every non-video key plus the tokens of
+ * its kept tiles; a non-video query attends to every key.  Softmax is exact
+ * over the keys a query attends to.
+ * q, k, v, out: bf16 [heads][tokens][128] in packed order, device pointers.
+ * INVALID_ARG also for tokens != prefix_tokens + frames*height*width, a
+ * non-positive grid or tile extent, or keep_frac outside (0, 1];
+ * UNSUPPORTED for another tile size or Tv > FVATTN_MAX_TILES.  Uses
+ * stream-ordered scratch: K and V in a padded tile layout (2 x heads x npad x
+ * 256 B, npad = prefix rounded up to 256 + Tv * tile size), tile means, the
+ * fp64 score matrix (heads x Tv x Tv), kept lists and per-block key lists. */
+int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, int heads,
+                       int tokens, int head_dim, float scale, int prefix_tokens, int frames,
+                       int height, int width, int tile_t, int tile_h, int tile_w,
+                       double keep_frac, void* stream);
+
+/* The selection of fvattn_forward_vsa alone: idx_out int32 [heads][Tv][k]
+ * (device), the kept video key tiles of every video query tile, ascending. */
+int fvattn_vsa_select(const void* q, const void* k, int heads, int tokens, int head_dim,
+                      int prefix_tokens, int frames, int height, int width, int tile_t, int tile_h,
+                      int tile_w, double keep_frac, int32_t* idx_out, void* stream);
+
+/* Number of video tiles Tv of a frames x height x width grid cut into
+ * tile_t x tile_h x tile_w tiles; -FVATTN_ERR_INVALID_ARG for a non-positive
+ * extent.  Pure host arithmetic. */
+int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int tile_h, int tile_w);
 
 /* Step S1 alone, for checking: fp64 tile means of x, bf16 [heads][tokens][128]
  * in, means_out fp64 [heads][T][128] out (device pointers). */

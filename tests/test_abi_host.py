@@ -217,3 +217,53 @@ def test_window_alloc_failure_hook(lib, monkeypatch):
     monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
     assert _win(lib) == fv.FVATTN_ERR_ALLOC
     assert _win(lib, q=NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
+def _vsa(lib, q=BOGUS, k=BOGUS, v=BOGUS, o=BOGUS, heads=4, prefix=37, grid=(5, 24, 42),
+         tile=(4, 4, 4), frac=0.1, scale=0.088, hd=128, tokens=None):
+    if tokens is None:
+        tokens = prefix + grid[0] * grid[1] * grid[2]
+    return lib.fvattn_forward_vsa(q, k, v, o, heads, tokens, hd, scale, prefix, *grid, *tile, frac, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(o=NULL), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(heads=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(prefix=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(grid=(0, 24, 42)), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(tile=(4, 0, 4)), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(tokens=5078), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(frac=0.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(frac=1.5), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(hd=64), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(tile=(2, 4, 4)), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(tile=(4, 8, 16)), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(grid=(400, 24, 42)), fv.FVATTN_ERR_UNSUPPORTED),      # 100 x 66 tiles > 2048
+])
+def test_forward_vsa_rejects_bad_arguments(lib, kw, want):
+    assert _vsa(lib, **kw) == want
+
+
+def test_vsa_entry_points_empty_and_counts(lib):
+    assert _vsa(lib, q=NULL, k=NULL, v=NULL, o=NULL, heads=0) == fv.FVATTN_OK
+    sel = lib.fvattn_vsa_select
+    assert sel(NULL, NULL, 0, 5077, 128, 37, 5, 24, 42, 4, 4, 4, 0.1, NULL, NULL) == fv.FVATTN_OK
+    assert sel(BOGUS, BOGUS, 2, 5077, 128, 37, 5, 24, 42, 4, 4, 4, 0.1, NULL, NULL) == \
+        fv.FVATTN_ERR_INVALID_ARG
+    assert sel(BOGUS, BOGUS, 2, 5078, 128, 37, 5, 24, 42, 4, 4, 4, 0.1, BOGUS, NULL) == \
+        fv.FVATTN_ERR_INVALID_ARG
+    tc = lib.fvattn_vsa_tile_count
+    assert tc(72, 24, 42, 4, 4, 4) == 1188
+    assert tc(102, 24, 42, 4, 4, 4) == 1716
+    assert tc(72, 24, 42, 4, 8, 8) == 324
+    assert tc(0, 24, 42, 4, 4, 4) == -fv.FVATTN_ERR_INVALID_ARG
+    for grid, tile in [((5, 24, 42), (4, 4, 4)), ((9, 7, 11), (2, 3, 5))]:
+        assert tc(*grid, *tile) == len(oracle.video_tiles(*grid, tile))
+
+
+def test_vsa_alloc_failure_hook(lib, monkeypatch):
+    monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
+    assert _vsa(lib) == fv.FVATTN_ERR_ALLOC
+    assert _vsa(lib, q=NULL) == fv.FVATTN_ERR_INVALID_ARG

@@ -254,6 +254,61 @@ def test_window_covering_everything_is_dense_bitwise(N, ft):
     assert torch.equal(a, b)
 
 
+# ------------------------------------------------------------------ VSA-H3 packed sequence
+
+VSA_CASES = [
+    # prefix, grid, tile, keep_frac
+    (0, (8, 8, 8), (4, 4, 4), 0.25),
+    (37, (5, 24, 42), (4, 4, 4), 0.1),
+    (300, (9, 24, 42), (4, 8, 8), 0.2),
+    (5, (4, 6, 10), (4, 4, 8), 0.3),
+    (600, (6, 10, 14), (2, 4, 8), 0.15),
+    (256, (3, 5, 7), (4, 4, 4), 0.5),
+]
+
+
+def _vsa_inputs(prefix, grid, heads, seed):
+    return inputs.make_packed_qkv(prefix, grid, heads, seed)
+
+
+@pytest.mark.parametrize("prefix,grid,tile,frac", VSA_CASES)
+def test_vsa_select_bit_exact(prefix, grid, tile, frac):
+    say("vsa select", prefix, grid, tile, frac)
+    q, k, v = _vsa_inputs(prefix, grid, 2, 400 + prefix)
+    got = fv.vsa_select(*to_dev(q, k), prefix, grid, tile, frac).cpu().numpy()
+    ref = oracle.vsa_select(oracle.widen(q), oracle.widen(k), prefix, grid, tile, frac)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("prefix,grid,tile,frac", VSA_CASES)
+def test_vsa_attention_matches_oracle(prefix, grid, tile, frac):
+    say("vsa attention", prefix, grid, tile, frac)
+    q, k, v = _vsa_inputs(prefix, grid, 2, 500 + prefix)
+    out = fv.forward_vsa(*to_dev(q, k, v), prefix, grid, tile, frac).cpu()
+    ref = oracle.vsa_attention(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128), prefix,
+                               grid, tile, frac)
+    assert_close(oracle.widen(out), ref, f"vsa prefix={prefix} grid={grid} tile={tile}")
+
+
+def test_vsa_keep_all_is_dense():
+    prefix, grid = 100, (5, 12, 14)
+    q, k, v = _vsa_inputs(prefix, grid, 2, 7)
+    out = fv.forward_vsa(*to_dev(q, k, v), prefix, grid, (4, 4, 4), 1.0).cpu()
+    ref = oracle.dense(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128))
+    assert_close(oracle.widen(out), ref, "vsa keep-all vs dense")
+
+
+def test_vsa_writes_every_row_and_nothing_else():
+    prefix, grid = 37, (5, 24, 42)
+    q, k, v = to_dev(*_vsa_inputs(prefix, grid, 2, 8))
+    N = q.shape[1]
+    buf = torch.full((2 * N + 64, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[:2 * N].view(2, N, 128)
+    fv.forward_vsa(q, k, v, prefix, grid, (4, 4, 4), 0.1, out=out)
+    assert not torch.isnan(out).any()
+    assert torch.isnan(buf[2 * N:]).all()
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")
@@ -336,3 +391,31 @@ def test_config4_window(cfg4):
 @pytest.mark.timeout(300)
 def test_config5_window(cfg5):
     _full_size_window(5, cfg5)
+
+
+@pytest.fixture(scope="module")
+def vsa72():
+    say("generating 512 + 72,576 packed x 16 inputs")
+    return inputs.make_packed_qkv(inputs.VSA_PREFIX, inputs.VSA_GRID_72, 16, 6)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("tile", [(4, 4, 4), (4, 8, 8)])
+def test_vsa_full_size(vsa72, tile):
+    prefix, grid, frac = inputs.VSA_PREFIX, inputs.VSA_GRID_72, 0.1
+    q, k, v = vsa72
+    qd, kd, vd = to_dev(q, k, v)
+    idx = fv.vsa_select(qd, kd, prefix, grid, tile, frac).cpu().numpy()
+    heads = [0, 7, 15]
+    ref_idx = oracle.vsa_select(*(oracle.widen(t[heads]) for t in (q, k)), prefix, grid, tile, frac)
+    assert np.array_equal(idx[heads], ref_idx)
+    say("vsa full size", tile, "selection bit-exact on heads", heads)
+    out = fv.forward_vsa(qd, kd, vd, prefix, grid, tile, frac)
+    N = q.shape[1]
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 1, prefix - 1, prefix, prefix + 1, prefix + 41, prefix + 42, prefix + 1007,
+                       prefix + 1008, N - 2, N - 1] + rng.integers(0, N, 24).tolist()))
+    got = out[heads][:, rows].cpu()
+    ref = oracle.vsa_attention(*(oracle.widen(t[heads]) for t in (q, k, v)), 1 / math.sqrt(128),
+                               prefix, grid, tile, frac, rows=rows, idx=ref_idx)
+    assert_close(oracle.widen(got), ref, f"vsa full size {tile}")

@@ -44,6 +44,9 @@ SIGNATURES = {
     "fvattn_forward_window": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fvattn_window_tiles": (_I, [_I, _I, _I, _I, _P, _P, _P]),
     "fvattn_tile_scores": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "fvattn_forward_vsa": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _I, _I, _I, _I, _D, _P]),
+    "fvattn_vsa_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _P, _P]),
+    "fvattn_vsa_tile_count": (_I, [_I, _I, _I, _I, _I, _I]),
     "fvattn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -239,3 +242,42 @@ def window_tiles(tokens: int, frame_tokens: int = 1008, chunk_frames: int = 5, n
         _check(load().fvattn_window_tiles(int(tokens), int(frame_tokens), int(chunk_frames),
                                           int(neighbours), _ptr(idx), _ptr(count), _stream_ptr(stream)))
     return idx, count
+
+
+def vsa_tile_count(grid, tile=(4, 4, 4)) -> int:
+    """fvattn_vsa_tile_count: video tiles of a (frames, height, width) grid."""
+    n = load().fvattn_vsa_tile_count(*(int(x) for x in grid), *(int(x) for x in tile))
+    if n < 0:
+        raise FvattnError(-n)
+    return n
+
+
+def forward_vsa(q, k, v, prefix: int, grid, tile=(4, 4, 4), keep_frac: float = 0.1,
+                scale: float | None = None, out=None, stream=None):
+    """fvattn_forward_vsa: VSA-H3 attention over [prefix | video grid] packed tokens."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_forward_vsa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, N, d, scale,
+                                         int(prefix), *(int(x) for x in grid),
+                                         *(int(x) for x in tile), float(keep_frac),
+                                         _stream_ptr(stream)))
+    return out
+
+
+def vsa_select(q, k, prefix: int, grid, tile=(4, 4, 4), keep_frac: float = 0.1, stream=None):
+    """fvattn_vsa_select: int32 [heads, Tv, keep] kept video key tiles per video query tile."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k)
+    tv = vsa_tile_count(grid, tile)
+    kk = keep_count(tv * TILE, keep_frac)    # the library's keep count of tv tiles
+    out = torch.empty((H, tv, kk), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_vsa_select(_ptr(q), _ptr(k), H, N, d, int(prefix),
+                                        *(int(x) for x in grid), *(int(x) for x in tile),
+                                        float(keep_frac), _ptr(out), _stream_ptr(stream)))
+    return out

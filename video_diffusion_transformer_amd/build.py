@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfvattn.so")
-SOURCES = ["attn_fwd.hip", "select.hip", "window.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "select.hip", "window.hip", "vsa.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -27,6 +27,7 @@ PER_FILE = {
     # the tile scores are defined with every product and sum rounded separately
     "select.hip": ["-ffp-contract=off"],
     "api.hip": ["-ffp-contract=off"],
+    "vsa.hip": ["-ffp-contract=off"],
 }
 
 

@@ -1,9 +1,9 @@
 // C ABI of the video-token attention library (declared in include/fvattn.h).
 //
 // Host side only: argument checks (all of them before any HIP call), the
-// keep count of compute_topk, stream-ordered scratch for the sparse mode, and
-// the head-group loop.  Every step of the computation runs in the kernels of
-// attn_fwd.hip and select.hip.
+// keep count of compute_topk, stream-ordered scratch for the sparse, window and
+// VSA-H3 modes, and the head-group loop.  Every step of the computation runs
+// in the kernels of attn_fwd.hip, select.hip, window.hip and vsa.hip.
 
 #include <math.h>
 #include <stdlib.h>
@@ -67,11 +67,13 @@ bool test_fail_alloc() {
 int hip_status(hipError_t e) { return e == hipSuccess ? FVATTN_OK : FVATTN_ERR_HIP; }
 
 // Scratch of one sparse call: tile means of Q [H][T][128], transposed tile
-// means of K [H][128][T], and the kept tile lists [H][T][keep].
+// means of K [H][128][T], the tile scores [H][T][T], and the kept tile lists
+// [H][T][keep].
 struct SparseScratch {
   void* base = nullptr;
   double* qm = nullptr;
   double* kmT = nullptr;
+  double* scores = nullptr;
   int32_t* idx = nullptr;
 };
 
@@ -80,9 +82,10 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_idx,
                   hipStream_t stream) {
   const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
+  const size_t scoreb = align256(sizeof(double) * (size_t)heads * tiles * tiles);
   const size_t idxb = need_idx ? align256(sizeof(int32_t) * (size_t)heads * tiles * keep) : 0;
   if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
-  if (hipMallocAsync(&s->base, 2 * means + idxb, stream) != hipSuccess) {
+  if (hipMallocAsync(&s->base, 2 * means + scoreb + idxb, stream) != hipSuccess) {
     (void)hipGetLastError();
     s->base = nullptr;
     return FVATTN_ERR_ALLOC;
@@ -90,7 +93,8 @@ int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_id
   char* p = (char*)s->base;
   s->qm = (double*)p;
   s->kmT = (double*)(p + means);
-  s->idx = need_idx ? (int32_t*)(p + 2 * means) : nullptr;
+  s->scores = (double*)(p + 2 * means);
+  s->idx = need_idx ? (int32_t*)(p + 2 * means + scoreb) : nullptr;
   return FVATTN_OK;
 }
 
@@ -105,7 +109,8 @@ int run_selection(const uint16_t* q, const uint16_t* k, int heads, int tokens, i
   const int T = tiles_of(tokens);
   hipError_t e = fvattn::launch_tile_means(q, s.qm, heads, tokens, false, stream);
   if (e == hipSuccess) e = fvattn::launch_tile_means(k, s.kmT, heads, tokens, true, stream);
-  if (e == hipSuccess) e = fvattn::launch_score_select(s.qm, s.kmT, heads, T, keep, idx, nullptr, stream);
+  if (e == hipSuccess) e = fvattn::launch_scores(s.qm, s.kmT, heads, T, s.scores, stream);
+  if (e == hipSuccess) e = fvattn::launch_select(s.scores, heads, T, keep, idx, stream);
   return hip_status(e);
 }
 
@@ -145,6 +150,42 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
   if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
   if (mode == FVATTN_BLOCK_SPARSE && tiles_of(tokens) > FVATTN_MAX_TILES)
     return FVATTN_ERR_UNSUPPORTED;
+  return FVATTN_OK;
+}
+
+// Checks shared by the VSA-H3 entry points, in the documented order; fills the
+// geometry.  Sets *empty when there is nothing to do.
+int check_vsa_args(int heads, int tokens, int head_dim, int prefix, int frames, int height,
+                   int width, int tt, int th, int tw, double keep_frac, fvattn::VsaGeom* g,
+                   bool* empty) {
+  *empty = false;
+  if (heads < 0 || tokens < 0 || prefix < 0 || frames < 1 || height < 1 || width < 1 || tt < 1 ||
+      th < 1 || tw < 1 || !keep_frac_ok(keep_frac))
+    return FVATTN_ERR_INVALID_ARG;
+  const long long video = (long long)frames * height * width;
+  if ((long long)prefix + video != (long long)tokens) return FVATTN_ERR_INVALID_ARG;
+  const long long size = (long long)tt * th * tw;
+  if (head_dim != kHeadDim || (size != 64 && size != 128 && size != 256))
+    return FVATTN_ERR_UNSUPPORTED;
+  g->prefix = prefix;
+  g->ppad = (prefix + 255) / 256 * 256;
+  g->frames = frames;
+  g->height = height;
+  g->width = width;
+  g->tt = tt;
+  g->th = th;
+  g->tw = tw;
+  g->nh = (height + th - 1) / th;
+  g->nw = (width + tw - 1) / tw;
+  g->size = (int)size;
+  const long long tiles = (long long)((frames + tt - 1) / tt) * g->nh * g->nw;
+  const long long npad = g->ppad + tiles * size;
+  if (tiles > FVATTN_MAX_TILES || npad / 64 > 8192 || npad * kHeadDim > kMaxPerHead)
+    return FVATTN_ERR_UNSUPPORTED;
+  g->tiles = (int)tiles;
+  g->npad = (int)npad;
+  g->tokens = tokens;
+  if (heads == 0) *empty = true;
   return FVATTN_OK;
 }
 
@@ -239,7 +280,7 @@ int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neig
   if (tiles_of(tokens) > FVATTN_MAX_TILES) return FVATTN_ERR_UNSUPPORTED;
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
-  fvattn::WindowParams wp;
+  fvattn::ListParams wp;
   wp.frame_tokens = frame_tokens;
   wp.chunk_frames = chunk_frames;
   wp.neighbours = neighbours;
@@ -273,7 +314,7 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   }
   int32_t* idx = (int32_t*)scratch;
   int32_t* counts = (int32_t*)((char*)scratch + idx_bytes);
-  fvattn::WindowParams wp;
+  fvattn::ListParams wp;
   wp.counts = counts;
   wp.frame_tokens = frame_tokens;
   wp.chunk_frames = chunk_frames;
@@ -320,9 +361,106 @@ int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles,
   }
   hipError_t e = fvattn::launch_transpose_means(km, (double*)kmT, heads, tiles, st);
   if (e == hipSuccess)
-    e = fvattn::launch_score_select(qm, (const double*)kmT, heads, tiles, 0, nullptr, scores_out, st);
+    e = fvattn::launch_scores(qm, (const double*)kmT, heads, tiles, scores_out, st);
   rc = hip_status(e);
   const int rf = hip_status(hipFreeAsync(kmT, st));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int tile_h, int tile_w) {
+  if (frames < 1 || height < 1 || width < 1 || tile_t < 1 || tile_h < 1 || tile_w < 1)
+    return -FVATTN_ERR_INVALID_ARG;
+  const long long t = (long long)((frames + tile_t - 1) / tile_t) * ((height + tile_h - 1) / tile_h) *
+                      ((width + tile_w - 1) / tile_w);
+  return t > 0x7fffffffLL ? -FVATTN_ERR_UNSUPPORTED : (int)t;
+}
+
+int fvattn_vsa_select(const void* q, const void* k, int heads, int tokens, int head_dim,
+                      int prefix_tokens, int frames, int height, int width, int tile_t, int tile_h,
+                      int tile_w, double keep_frac, int32_t* idx_out, void* stream) {
+  fvattn::VsaGeom g;
+  bool empty;
+  int rc = check_vsa_args(heads, tokens, head_dim, prefix_tokens, frames, height, width, tile_t,
+                          tile_h, tile_w, keep_frac, &g, &empty);
+  if (rc != FVATTN_OK || empty) return rc;
+  if (!q || !k || !idx_out) return FVATTN_ERR_INVALID_ARG;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int keep = keep_of(g.tiles, keep_frac);
+  const size_t means = align256(sizeof(double) * (size_t)heads * g.tiles * kHeadDim);
+  const size_t scoreb = align256(sizeof(double) * (size_t)heads * g.tiles * g.tiles);
+  void* base = nullptr;
+  if (hipMallocAsync(&base, 2 * means + scoreb, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  double* qm = (double*)base;
+  double* kmT = (double*)((char*)base + means);
+  double* scores = (double*)((char*)base + 2 * means);
+  hipError_t e = fvattn::launch_vsa_means((const uint16_t*)q, qm, g, heads, false, st);
+  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)k, kmT, g, heads, true, st);
+  if (e == hipSuccess) e = fvattn::launch_scores(qm, kmT, heads, g.tiles, scores, st);
+  if (e == hipSuccess) e = fvattn::launch_select(scores, heads, g.tiles, keep, idx_out, st);
+  rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(base, st));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, int heads,
+                       int tokens, int head_dim, float scale, int prefix_tokens, int frames,
+                       int height, int width, int tile_t, int tile_h, int tile_w, double keep_frac,
+                       void* stream) {
+  if (!scale_ok(scale)) return FVATTN_ERR_INVALID_ARG;
+  fvattn::VsaGeom g;
+  bool empty;
+  int rc = check_vsa_args(heads, tokens, head_dim, prefix_tokens, frames, height, width, tile_t,
+                          tile_h, tile_w, keep_frac, &g, &empty);
+  if (rc != FVATTN_OK || empty) return rc;
+  if (!q || !k || !v || !out) return FVATTN_ERR_INVALID_ARG;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int keep = keep_of(g.tiles, keep_frac);
+  const int blocks = (g.npad + 255) / 256, nsub = g.npad / 64;
+  const size_t packed = align256(sizeof(uint16_t) * (size_t)heads * g.npad * kHeadDim);
+  const size_t means = align256(sizeof(double) * (size_t)heads * g.tiles * kHeadDim);
+  const size_t idxb = align256(sizeof(int32_t) * (size_t)heads * g.tiles * keep);
+  const size_t listb = align256(sizeof(int32_t) * (size_t)heads * blocks * nsub);
+  const size_t cntb = align256(sizeof(int32_t) * (size_t)heads * blocks);
+  const size_t scoreb = align256(sizeof(double) * (size_t)heads * g.tiles * g.tiles);
+  void* base = nullptr;
+  if (hipMallocAsync(&base, 2 * packed + 2 * means + idxb + listb + cntb + scoreb, st) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  char* p = (char*)base;
+  uint16_t* kp = (uint16_t*)p;
+  uint16_t* vp = (uint16_t*)(p + packed);
+  double* qm = (double*)(p + 2 * packed);
+  double* kmT = (double*)(p + 2 * packed + means);
+  int32_t* idx = (int32_t*)(p + 2 * packed + 2 * means);
+  int32_t* lists = (int32_t*)(p + 2 * packed + 2 * means + idxb);
+  int32_t* counts = (int32_t*)(p + 2 * packed + 2 * means + idxb + listb);
+  double* scores = (double*)(p + 2 * packed + 2 * means + idxb + listb + cntb);
+  hipError_t e = fvattn::launch_vsa_pack((const uint16_t*)k, (const uint16_t*)v, kp, vp, g, heads, st);
+  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)q, qm, g, heads, false, st);
+  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)k, kmT, g, heads, true, st);
+  if (e == hipSuccess) e = fvattn::launch_scores(qm, kmT, heads, g.tiles, scores, st);
+  if (e == hipSuccess) e = fvattn::launch_select(scores, heads, g.tiles, keep, idx, st);
+  if (e == hipSuccess) e = fvattn::launch_vsa_lists(idx, keep, g, heads, lists, counts, st);
+  if (e == hipSuccess) {
+    fvattn::ListParams lp;
+    lp.counts = counts;
+    lp.vsa = g;
+    e = fvattn::launch_attention_vsa((const uint16_t*)q, kp, vp, (uint16_t*)out, lists, lp, heads,
+                                     scale, st);
+  }
+  rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(base, st));
   return rc != FVATTN_OK ? rc : rf;
 }
 

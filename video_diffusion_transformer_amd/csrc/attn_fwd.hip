@@ -124,19 +124,22 @@ using Buf = std::integral_constant<int, B>;
 // The body lives in a __device__ template so that only the device compilation
 // instantiates it; the __global__ wrapper below is all the host side sees.
 // kMode: 0 dense, 1 per-head kept-tile lists of `keep` tiles, 2 frame-window
-// lists shared by all heads (per-row counts, per-element frame mask).
+// lists shared by all heads (per-block counts, per-element frame mask), 3
+// VSA-H3 per-head lists of 64-key sub-tiles over the padded tile layout (Q
+// gathered from and O scattered to the packed token order).
 template <int kMode, int kWaves, int kStages, int kQB, int kBN>
 __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                                               const uint16_t* __restrict__ K,
                                               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                               const int32_t* __restrict__ idx, int keep, int N,
-                                              int qtiles, float c, WindowParams wp) {
+                                              int qtiles, float c, ListParams wp) {
   constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
   constexpr int kTileBytes = kBN * kRowBytes; // one K or V stage
   constexpr int kBM = 32 * kQB * kWaves;
   constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
   constexpr int kPrefetch = kStages - 1;
   static_assert(kMode != 1 || kBM == kTile, "per-head lists cover one selection tile");
+  static_assert(kMode != 3 || (kBN == 64 && kBM == 256), "VSA entries are 64-key stages of 256-row blocks");
   // One LDS array per slot: distinct objects let the compiler see that a read
   // of one slot cannot alias a buffer-to-LDS load still landing in another,
   // so it does not wait for every load in flight before each LDS read.
@@ -157,12 +160,29 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   const size_t hoff = (size_t)h * (size_t)N * kHeadDim;
   const uint16_t* Kh = K + hoff;
   const uint16_t* Vh = V + hoff;
+  // VSA: N counts padded slots; Q and O keep the packed token order
+  const int qn = kMode == 3 ? wp.vsa.tokens : N;
+  const size_t qoff = (size_t)h * (size_t)qn * kHeadDim;
 
   // Q^T fragments of this lane's two query rows (B operands of S^T = K Q^T):
   // qf[qb][dk][i] = Q[q0 + 32 qb + l32][16 dk + 8 g + i]; rows past N read as 0.
   const int q0 = qt * kBM + wave * 32 * kQB;
   bf16x8 qf[kQB][8];
-  {
+  if constexpr (kMode == 3) {
+    // gather: the lane's slot holds token vsa_slot_token(slot); padding reads
+    // past the end of the descriptor and gets zeros
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, qn * kRowBytes);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int tok = vsa_slot_token(wp.vsa, q0 + 32 * qb + l32);
+      const int row_off = (tok < 0 ? qn : tok) * kRowBytes;
+#pragma unroll
+      for (int dk = 0; dk < 8; ++dk) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, row_off + 32 * dk + 16 * g, 0, 0);
+        qf[qb][dk] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  } else {
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
 #pragma unroll
@@ -178,21 +198,24 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   const int ktiles = (N + kTile - 1) / kTile;
   const int32_t* irow = kMode == 1   ? idx + ((size_t)h * qtiles + qt) * keep
                         : kMode == 2 ? idx + (size_t)qt * ktiles
+                        : kMode == 3 ? idx + ((size_t)h * qtiles + qt) * (N / kBN)
                                      : nullptr;
-  const int nsub = kMode == 0 ? (N + kBN - 1) / kBN
-                              : (kTile / kBN) * (kMode == 1 ? keep : wp.counts[qt]);
+  const int nsub = kMode == 0   ? (N + kBN - 1) / kBN
+                   : kMode == 3 ? wp.counts[(size_t)h * qtiles + qt]
+                                : (kTile / kBN) * (kMode == 1 ? keep : wp.counts[qt]);
   // List entry of stage i (any i >= 0: past the end it repeats the last
   // entry, so the load never leaves the list), and the first key of stage i
   // from its entry.  Window lists flag (kMaskFlag) the key tiles that need
   // per-element masking for some row of this block; kv_of passes the flag on.
-  constexpr int kSub = kTile / kBN;   // stages per key tile
-  const int nlist = kMode == 1 ? keep : kMode == 2 ? wp.counts[qt] : 1;
+  constexpr int kSub = kMode == 3 ? 1 : kTile / kBN;   // stages per list entry
+  const int nlist = kMode == 1 ? keep : kMode == 2 ? wp.counts[qt] : kMode == 3 ? nsub : 1;
   auto entry = [&](int i) -> int {
     const int j = i / kSub;
     return irow[j < nlist ? j : nlist - 1];
   };
   auto kv_of = [&](int e, int i) -> int {
     if (kMode == 0) return i * kBN;
+    if (kMode == 3) return (e & 0xffff) * kBN | (e & kMaskFlag);
     const int flag = kMode == 2 ? (e & kMaskFlag) : 0;
     int t = kMode == 2 ? (e & ~kMaskFlag) : e;
     t = t < 0 ? 0 : (t >= ktiles ? ktiles - 1 : t);
@@ -264,7 +287,13 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
   float m_run[kQB], l_run[kQB];
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+  // VSA lists can open with stages a wave does not attend to (masked whole):
+  // a finite start keeps exp2(S c - m) at exp2(-inf) = 0 there, where -inf
+  // would give exp2(NaN).  The first real stage replaces it (alpha = 0).
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = kMode == 3 ? -1e30f : -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
   // S^T of one stage: S[qb][kb][r] = S[q0 + 32 qb + l32][kv0 + 32 kb + 16 g + r]
   auto qk = [&](auto bufc, f32x16 (&S)[kQB][kKB]) {
@@ -337,6 +366,30 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
         for (int qb = 0; qb < kQB; ++qb)
           if (key >= N || !(key < next_frame ? ok0[qb] : ok1[qb])) S[qb][kb][r] = -INFINITY;
       }
+  };
+  // VSA (kMode 3), flagged entries only: a wave whose 64-row query group does
+  // not attend to the sub-tile masks the whole stage; otherwise keys past the
+  // sub-tile's valid count (padding slots) are masked.
+  auto vsa_mask = [&](f32x16 (&S)[kQB][kKB], int e) {
+    if (!((e >> (kVsaGroupShift + (wave >> 1))) & 1)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[qb][kb][r] = -INFINITY;
+      return;
+    }
+    const int n = ((e >> kVsaCountShift) & 63) + 1;
+    if (n == kBN) return;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + 16 * g + r >= n) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) S[qb][kb][r] = -INFINITY;
+        }
   };
   // Row max of a stage, in scaled log2 units.
   auto rowmax = [&](const f32x16 (&S)[kQB][kKB], float (&mx)[kQB]) {
@@ -466,6 +519,8 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 
     if constexpr (kMode == 2) {
       if (has_next && (kv_next & kMaskFlag)) window_mask(Snext, kv_next & ~kMaskFlag);
+    } else if constexpr (kMode == 3) {
+      if (has_next && (kv_next & kMaskFlag)) vsa_mask(Snext, ring[0]);
     } else if (has_next && kv_next + kBN > N) {
       mask(Snext, kv_next);
     }
@@ -515,6 +570,8 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     qk(Buf<0>(), SA);
     if constexpr (kMode == 2) {
       if (kv0e & kMaskFlag) window_mask(SA, kv0);
+    } else if constexpr (kMode == 3) {
+      if (kv0e & kMaskFlag) vsa_mask(SA, entry(0));
     }
     else if (kv0 + kBN > N) mask(SA, kv0);
     float mx[kQB];
@@ -537,8 +594,9 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   for (int qb = 0; qb < kQB; ++qb) {
     const float inv = 1.f / halfwave_sum(l_run[qb]);
     const int qrow = q0 + 32 * qb + l32;
-    if (qrow < N) {
-      uint16_t* orow = O + hoff + (size_t)qrow * kHeadDim;
+    const int orow_idx = kMode == 3 ? vsa_slot_token(wp.vsa, qrow) : (qrow < N ? qrow : -1);
+    if (orow_idx >= 0) {
+      uint16_t* orow = O + qoff + (size_t)orow_idx * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -565,7 +623,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3 -
 attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 const int32_t* __restrict__ idx, int keep, int N, int qtiles, float c,
-                WindowParams wp) {
+                ListParams wp) {
   attn_fwd_body<kMode, kWaves, kStages, kQB, kBN>(Q, K, V, O, idx, keep, N, qtiles, c, wp);
 }
 
@@ -581,7 +639,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
     attn_fwd_kernel<1, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        q, k, v, out, idx, keep, tokens, qtiles, c, WindowParams{});
+        q, k, v, out, idx, keep, tokens, qtiles, c, ListParams{});
   } else {
     // 256 query rows per workgroup (8 waves) share each K/V stage; one
     // workgroup per CU leaves LDS for three slots, loads two stages ahead
@@ -589,13 +647,13 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
     attn_fwd_kernel<0, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
-        q, k, v, out, idx, keep, tokens, qtiles, c, WindowParams{});
+        q, k, v, out, idx, keep, tokens, qtiles, c, ListParams{});
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   uint16_t* out, const int32_t* idx, const WindowParams& wp,
+                                   uint16_t* out, const int32_t* idx, const ListParams& wp,
                                    int heads, int tokens, float scale, hipStream_t stream) {
   // the dense shape: 256 query rows per workgroup (8 waves); idx and
   // wp.counts hold one list per 256-row block (kWindowRows)
@@ -605,6 +663,20 @@ hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const u
   if (blocks <= 0) return hipSuccess;
   attn_fwd_kernel<2, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
       q, k, v, out, idx, 0, tokens, qtiles, c, wp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_vsa(const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
+                                uint16_t* out, const int32_t* lists, const ListParams& lp,
+                                int heads, float scale, hipStream_t stream) {
+  // the dense shape: 256 padded query slots per workgroup (8 waves), one list
+  // of 64-key sub-tiles per (head, block)
+  const float c = scale * 1.4426950408889634f;  // scale * log2(e)
+  const int qtiles = (lp.vsa.npad + 255) / 256;
+  const long long blocks = (long long)heads * qtiles;
+  if (blocks <= 0) return hipSuccess;
+  attn_fwd_kernel<3, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+      q, kp, vp, out, lists, 0, lp.vsa.npad, qtiles, c, lp);
   return hipGetLastError();
 }
 

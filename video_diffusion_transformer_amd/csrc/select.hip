@@ -9,15 +9,17 @@
 //     dimensions of one tile and adds its tokens one after another), then one
 //     IEEE-correct fp64 division by the number of valid tokens.  HBM-bound: it
 //     reads Q and K once with 128-bit loads, 16 lanes per 256-byte token row.
-// S2  score_select_kernel: sigma_ij = sum_d qm_i[d] * km_j[d] in fp64 from +0.0
-//     in order d = 0..127, every product and every sum rounded on its own
-//     (fp contraction is off in this file).  One workgroup owns 8 query tiles of
-//     one head; their means sit in LDS and every thread walks one key tile
-//     column of the transposed key means (coalesced), keeping 8 scores.
-// S3  per query tile, the `keep` largest scores, ties to the lower key tile,
-//     found by one wave with a most-significant-bit-first radix select on the
-//     order-preserving 64-bit image of the doubles, then emitted in ascending
-//     tile order with ballots.
+// S2  scores_kernel: sigma_ij = sum_d qm_i[d] * km_j[d] in fp64 from +0.0 in
+//     order d = 0..127, every product and every sum rounded on its own (fp
+//     contraction is off in this file).  A workgroup owns a 64 x 64 block of
+//     (query tile, key tile) pairs; the means pass through LDS in chunks of 32
+//     dimensions and every thread keeps a 4 x 4 block of running sums in
+//     registers, each summed in the canonical order.  The scores go to a
+//     stream-ordered scratch matrix [heads][T][T].
+// S3  select_kernel: per query tile, the `keep` largest scores, ties to the
+//     lower key tile, found by one wave with a most-significant-bit-first radix
+//     select on the order-preserving 64-bit image of the doubles, then emitted
+//     in ascending tile order with ballots.
 
 #include "fvattn_internal.h"
 
@@ -29,8 +31,8 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMeansTiles = 16;   // tiles per workgroup in S1 (16 threads per tile)
-constexpr int kRows = 8;          // query tiles per workgroup in S2/S3
-constexpr int kMaxM = 32;         // FVATTN_MAX_TILES / 64 score slots per lane
+constexpr int kBlk = 64;          // S2: query and key tiles per workgroup
+constexpr int kChunk = 32;        // S2: dimensions staged per pass
 
 __device__ __forceinline__ double bf16_lo(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ __forceinline__ double bf16_hi(uint32_t w) {
@@ -93,7 +95,8 @@ __device__ __forceinline__ uint64_t order_key(double x) {
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
 // One wave: the `keep` largest of sc[0..T) (ties -> lower index), written
-// ascending to out[0..keep).
+// ascending to out[0..keep).  T <= 64 kMaxM.
+template <int kMaxM>
 __device__ void select_row(const double* sc, int T, int keep, int32_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -154,45 +157,62 @@ __device__ void select_row(const double* sc, int T, int keep, int32_t* __restric
   }
 }
 
-template <bool kWriteScores>
-__global__ __launch_bounds__(256) void score_select_kernel(const double* __restrict__ qm,
-                                                           const double* __restrict__ kmT, int T,
-                                                           int keep, int32_t* __restrict__ idx,
-                                                           double* __restrict__ scores) {
-  extern __shared__ double sh[];
-  double* qs = sh;                        // [128][kRows]
-  double* sc = sh + kHeadDim * kRows;     // [kRows][T]
-  const int h = blockIdx.y, i0 = blockIdx.x * kRows;
-  const int nrows = (T - i0 < kRows) ? T - i0 : kRows;
-  const int tid = threadIdx.x;
-  for (int x = tid; x < kHeadDim * kRows; x += 256) {
-    const int d = x / kRows, r = x - d * kRows;
-    qs[x] = (r < nrows) ? qm[((size_t)h * T + i0 + r) * kHeadDim + d] : 0.0;
-  }
-  __syncthreads();
+__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qm,
+                                                     const double* __restrict__ kmT, int T,
+                                                     double* __restrict__ scores) {
+  __shared__ double qs[kChunk][kBlk];   // qs[d][i]: query means of the block, this chunk
+  __shared__ double ks[kChunk][kBlk];   // ks[d][j]: key means of the block, this chunk
+  const int h = blockIdx.z, i0 = blockIdx.y * kBlk, j0 = blockIdx.x * kBlk;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const double* qh = qm + (size_t)h * T * kHeadDim;
   const double* kh = kmT + (size_t)h * kHeadDim * T;
-  for (int j = tid; j < T; j += 256) {
-    double acc[kRows];
+  double acc[4][4];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) acc[r] = 0.0;
-#pragma unroll 8
-    for (int d = 0; d < kHeadDim; ++d) {
-      const double kv = kh[(size_t)d * T + j];
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[r] = acc[r] + qs[d * kRows + r] * kv;
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int d0 = 0; d0 < kHeadDim; d0 += kChunk) {
+    __syncthreads();
+    for (int x = tid; x < kChunk * kBlk; x += 256) {
+      // query means: row i0 + (x / kChunk), dimension d0 + x % kChunk (row-major reads)
+      const int r = x / kChunk, d = x - r * kChunk;
+      qs[d][r] = (i0 + r < T) ? qh[(size_t)(i0 + r) * kHeadDim + d0 + d] : 0.0;
+      // key means: dimension d0 + x / kBlk, tile j0 + x % kBlk (transposed: row-major reads)
+      const int dd = x / kBlk, c = x - dd * kBlk;
+      ks[dd][c] = (j0 + c < T) ? kh[(size_t)(d0 + dd) * T + j0 + c] : 0.0;
     }
-    if (kWriteScores) {
-      for (int r = 0; r < nrows; ++r) scores[((size_t)h * T + i0 + r) * T + j] = acc[r];
-    } else {
+    __syncthreads();
+#pragma unroll 4
+    for (int d = 0; d < kChunk; ++d) {
+      double qv[4], kv[4];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) sc[r * T + j] = acc[r];
+      for (int a = 0; a < 4; ++a) qv[a] = qs[d][4 * ty + a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) kv[b] = ks[d][4 * tx + b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = acc[a][b] + qv[a] * kv[b];
     }
   }
-  if (kWriteScores) return;
-  __syncthreads();
-  const int wave = tid >> 6;
-  for (int r = wave; r < nrows; r += 4)
-    select_row(sc + r * T, T, keep, idx + ((size_t)h * T + i0 + r) * keep);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + 4 * ty + a;
+    if (i >= T) continue;
+    double* row = scores + ((size_t)h * T + i) * T;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (j0 + 4 * tx + b < T) row[j0 + 4 * tx + b] = acc[a][b];
+  }
+}
+
+// One wave per (head, query tile) row of the score matrix; 4 rows per workgroup.
+template <int kMaxM>
+__global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ scores, int T,
+                                                     int rows, int keep, int32_t* __restrict__ idx) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  select_row<kMaxM>(scores + (size_t)row * T, T, keep, idx + (size_t)row * keep);
 }
 
 __global__ void transpose_means_kernel(const double* __restrict__ in, double* __restrict__ out,
@@ -218,25 +238,35 @@ hipError_t launch_tile_means(const uint16_t* x, double* out, int heads, int toke
   return hipGetLastError();
 }
 
-hipError_t launch_score_select(const double* qm, const double* kmT, int heads, int tiles,
-                               int keep, int32_t* idx_out, double* scores_out,
-                               hipStream_t stream) {
+hipError_t launch_scores(const double* qm, const double* kmT, int heads, int tiles,
+                         double* scores_out, hipStream_t stream) {
   if (heads <= 0 || tiles <= 0) return hipSuccess;
-  const dim3 grid((tiles + kRows - 1) / kRows, heads);
-  if (scores_out) {
-    const size_t lds = sizeof(double) * kHeadDim * kRows;
-    hipLaunchKernelGGL(score_select_kernel<true>, grid, dim3(256), lds, stream, qm, kmT, tiles,
-                       keep, idx_out, scores_out);
-  } else {
-    const size_t lds = sizeof(double) * ((size_t)kHeadDim * kRows + (size_t)kRows * tiles);
-    if (lds > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute((const void*)score_select_kernel<false>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(score_select_kernel<false>, grid, dim3(256), lds, stream, qm, kmT, tiles,
-                       keep, idx_out, scores_out);
-  }
+  const int nb = (tiles + kBlk - 1) / kBlk;
+  hipLaunchKernelGGL(scores_kernel, dim3(nb, nb, heads), dim3(256), 0, stream, qm, kmT, tiles,
+                     scores_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const double* scores, int heads, int tiles, int keep, int32_t* idx_out,
+                         hipStream_t stream) {
+  if (heads <= 0 || tiles <= 0) return hipSuccess;
+  const int rows = heads * tiles;
+  const dim3 grid((rows + 3) / 4), block(256);
+  // the smallest slot count that holds a row (register use grows with it)
+  if (tiles <= 8 * 64)
+    hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else if (tiles <= 16 * 64)
+    hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else if (tiles <= 20 * 64)
+    hipLaunchKernelGGL(select_kernel<20>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else if (tiles <= 24 * 64)
+    hipLaunchKernelGGL(select_kernel<24>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else if (tiles <= 28 * 64)
+    hipLaunchKernelGGL(select_kernel<28>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else if (tiles <= 32 * 64)
+    hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, stream, scores, tiles, rows, keep, idx_out);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

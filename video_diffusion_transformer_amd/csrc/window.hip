@@ -22,7 +22,7 @@
 namespace fvattn {
 namespace {
 
-__global__ __launch_bounds__(64) void window_tiles_kernel(int N, WindowParams wp, int q_rows,
+__global__ __launch_bounds__(64) void window_tiles_kernel(int N, ListParams wp, int q_rows,
                                                           bool flags, int T,
                                                           int32_t* __restrict__ idx,
                                                           int32_t* __restrict__ counts) {
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64) void window_tiles_kernel(int N, WindowParams wp
 
 }  // namespace
 
-hipError_t launch_window_tiles(int tokens, const WindowParams& wp, int q_rows, bool flags,
+hipError_t launch_window_tiles(int tokens, const ListParams& wp, int q_rows, bool flags,
                                int32_t* idx, int32_t* counts, hipStream_t stream) {
   const int T = (tokens + kTile - 1) / kTile;
   const int blocks = (tokens + q_rows - 1) / q_rows;

@@ -121,3 +121,24 @@ def make_inputs(config_id: int, heads: int | None = None):
     (the first ``heads`` of the same seeded streams)."""
     c = CONFIGS[config_id]
     return make_qkv(c.tokens, c.heads if heads is None else heads, c.dist, c.seed)
+
+
+# Packed-sequence workload of VSA-H3 (FastH3 page, "Lever two"): a non-video
+# prefix (text, condition keyframes, audio) ahead of the generated video.  The
+# pages give no prefix length; 512 tokens is this stand-in's choice.
+VSA_PREFIX = 512
+VSA_GRID_72 = (72, 24, 42)       # 72,576 video tokens (10 s clip)
+
+
+def make_packed_qkv(prefix: int, grid, heads: int, seed: int):
+    """(q, k, v) CPU bf16 [heads][prefix + frames*height*width][128]: an i.i.d.
+    prefix followed by frame-correlated video tokens in (t, h, w) raster order
+    (the video part is make_qkv's "frame" recipe with frames of height*width
+    tokens; the prefix draws from the streams of seed + 1000)."""
+    frames, height, width = grid
+    vq, vk, vv = make_qkv(frames * height * width, heads, "frame", seed,
+                          frame_tokens=height * width)
+    if prefix == 0:
+        return vq, vk, vv
+    pq, pk, pv = make_qkv(prefix, heads, "iid", seed + 1000)
+    return tuple(torch.cat([a, b], dim=1).contiguous() for a, b in ((pq, vq), (pk, vk), (pv, vv)))
