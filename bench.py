@@ -130,7 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa"], default=None,
+    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8"], default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
                          "0 for window and vsa, which are timed outside the step)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,6 +183,7 @@ def main():
     do_sparse = args.only in (None, "sparse")
     do_window = args.only in (None, "window")
     do_vsa = args.only in (None, "vsa")
+    do_int8 = args.only in (None, "int8")
     if not do_dense:
         flop_dense = 0.0
     if not do_sparse:
@@ -258,6 +259,30 @@ def main():
                   "tflops_effective": round(flop_w / (wm * 1e-3) / 1e12, 2),
                   "tflops_visited": round(flop_w_visited / (wm * 1e-3) / 1e12, 2),
                   "density": round(flop_w / (4.0 * TOKENS * TOKENS * 128 * HEADS), 4)}
+
+    # dense attention with INT8 query-key scores, outside the step: same
+    # inputs, same head groups
+    int8 = None
+    if do_int8:
+        out_i8 = torch.empty_like(qd)
+        i_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        i_ms = []
+        for i in range(4):
+            i_ev[0].record(stream)
+            fv.forward_heads(qd, kd, vd, GROUP, scale=scale, mode="int8", out=out_i8)
+            i_ev[1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                i_ms.append(i_ev[0].elapsed_time(i_ev[1]))
+        im = float(np.median(i_ms))
+        flop_i = 4.0 * TOKENS * TOKENS * 128 * HEADS
+        int8 = {"ms": round(im, 3), "tflops": round(flop_i / (im * 1e-3) / 1e12, 2),
+                "frac_peak_bf16": round(flop_i / (im * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if do_dense:
+            # output difference against the bf16 dense path on the same inputs
+            d = (out_i8.float() - out_dense.float())
+            int8["rel_diff_vs_bf16_dense"] = round(float(d.norm() / out_dense.float().norm()), 5)
+        del out_i8
 
     # VSA-H3 packed sequence, outside the step: a 512-token non-video prefix
     # ahead of the same 72 x 24 x 42 video grid, (4, 4, 4) tiles, 90% sparse,
@@ -343,6 +368,10 @@ def main():
         result["window"] = window
     if vsa is not None:
         result["vsa"] = vsa
+    if int8 is not None:
+        if do_dense:
+            int8["speedup_vs_dense"] = round(d_ms / int8["ms"], 3)
+        result["int8"] = int8
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), budget", args.cpu_budget, "s")
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)

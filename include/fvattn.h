@@ -13,7 +13,7 @@
  * materialized (FreeVideo page, section "Why it does not fit: the
  * arithmetic").
  *
- * Two modes:
+ * Three modes:
  *   FVATTN_DENSE         out = softmax(scale * Q K^T) V over every key.
  *   FVATTN_BLOCK_SPARSE  the sequence is cut into contiguous 128-token tiles;
  *                        tiles are mean-pooled, every query tile scores every
@@ -22,6 +22,17 @@
  *                        kept (compute_topk, FastH3 page, "Lever two"), and
  *                        exact attention runs over the kept tiles only, the
  *                        softmax normalized over the kept keys.
+ *   FVATTN_DENSE_INT8QK  FVATTN_DENSE with the scores from INT8 queries and
+ *                        keys (FastH3 page, section "Update: consumer GPUs
+ *                        and Trim", subsection "Per device"): symmetric codes
+ *                        in [-127, 127], scale = max |x| / 127 (1 for a group
+ *                        of zeros) per query row and per block of 64
+ *                        consecutive keys of a head, code = round-half-to-even
+ *                        (x / scale) with a correctly rounded float32 scale
+ *                        and division; score = scale * sq * sk * (exact
+ *                        integer dot product).  V and P V stay bf16 as in
+ *                        FVATTN_DENSE.  Uses stream-ordered scratch for the
+ *                        key codes and scales (heads * tokens * 128 bytes).
  *
  * Selection rule, exactly (the pages leave these points open; this is the
  * library's definition): tile t covers tokens [128t, min(128t+128, N)) and has
@@ -82,7 +93,7 @@ typedef enum {
   FVATTN_ERR_HIP = 4
 } fvattn_status;
 
-typedef enum { FVATTN_DENSE = 0, FVATTN_BLOCK_SPARSE = 1 } fvattn_mode;
+typedef enum { FVATTN_DENSE = 0, FVATTN_BLOCK_SPARSE = 1, FVATTN_DENSE_INT8QK = 2 } fvattn_mode;
 
 #define FVATTN_TILE 128       /* tokens per selection tile */
 #define FVATTN_HEAD_DIM 128   /* the only supported head width */
@@ -190,6 +201,12 @@ int fvattn_vsa_select(const void* q, const void* k, int heads, int tokens, int h
  * tile_t x tile_h x tile_w tiles; -FVATTN_ERR_INVALID_ARG for a non-positive
  * extent.  Pure host arithmetic. */
 int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int tile_h, int tile_w);
+
+/* The key quantization of FVATTN_DENSE_INT8QK alone, for checking: k bf16
+ * [heads][tokens][128] in; codes_out int8 [heads][tokens][128] and
+ * scales_out float [heads][ceil(tokens / 64)] out (device pointers). */
+int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
+                      float* scales_out, void* stream);
 
 /* Step S1 alone, for checking: fp64 tile means of x, bf16 [heads][tokens][128]
  * in, means_out fp64 [heads][T][128] out (device pointers). */

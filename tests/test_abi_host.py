@@ -267,3 +267,21 @@ def test_vsa_alloc_failure_hook(lib, monkeypatch):
     monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
     assert _vsa(lib) == fv.FVATTN_ERR_ALLOC
     assert _vsa(lib, q=NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
+def test_int8_mode_argument_checks(lib, monkeypatch):
+    # mode 2 (dense, INT8 query-key scores): keep_frac is not looked at
+    assert _fwd(lib, q=NULL, mode=2, frac=float("nan")) == fv.FVATTN_ERR_INVALID_ARG
+    assert _fwd(lib, mode=2, hd=64) == fv.FVATTN_ERR_UNSUPPORTED
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0, mode=2) == fv.FVATTN_OK
+    assert _fwd(lib, mode=3) == fv.FVATTN_ERR_INVALID_ARG
+    qk = lib.fvattn_quantize_k
+    assert qk(NULL, 0, 100, 128, NULL, NULL, NULL) == fv.FVATTN_OK
+    assert qk(BOGUS, 2, 100, 128, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert qk(BOGUS, 2, 100, 128, BOGUS, NULL, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert qk(BOGUS, 2, 100, 96, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert qk(BOGUS, -2, 100, 128, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
+    assert _fwd(lib, mode=2) == fv.FVATTN_ERR_ALLOC
+    assert lib.fvattn_forward_heads(BOGUS, BOGUS, BOGUS, BOGUS, 56, 16, 1008, 128, 0.088, 2, 0.1,
+                                    NULL) == fv.FVATTN_ERR_ALLOC

@@ -309,6 +309,41 @@ def test_vsa_writes_every_row_and_nothing_else():
     assert torch.isnan(buf[2 * N:]).all()
 
 
+# ------------------------------------------------------------------ INT8 query-key scores
+
+@pytest.mark.parametrize("N,dist", [(1, "iid"), (63, "iid"), (64, "iid"), (65, "iid"), (1000, "iid"),
+                                    (5040, "frame"), (72576, "frame")])
+def test_quantize_k_bit_exact(N, dist):
+    say("quantize k", N, dist)
+    _, k, _ = inputs.make_qkv(N, 2, dist, 700 + N)
+    codes, scales = fv.quantize_k(k.to(DEV))
+    for h in range(2):
+        ref_c, ref_s = oracle.quantize_blocks(oracle.widen(k[h]))
+        assert np.array_equal(scales[h].cpu().numpy(), ref_s)
+        assert np.array_equal(codes[h].cpu().numpy().astype(np.int64), ref_c)
+
+
+@pytest.mark.parametrize("N,dist", [(1, "iid"), (5, "iid"), (64, "iid"), (65, "iid"), (129, "iid"),
+                                    (300, "iid"), (1000, "iid"), (1008, "frame"), (5040, "frame")])
+def test_int8_attention_matches_oracle(N, dist):
+    say("int8 attention", N, dist)
+    q, k, v = inputs.make_qkv(N, 2, dist, 800 + N)
+    out = fv.forward(*to_dev(q, k, v), mode="int8").cpu()
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    ref = oracle.int8_scores_attention(qw, kw, vw, 1 / math.sqrt(128))
+    assert_close(oracle.widen(out), ref, f"int8 N={N}")
+    dense = oracle.dense(qw, kw, vw, 1 / math.sqrt(128))
+    say(f"int8 N={N}: relative error against exact dense "
+        f"{np.linalg.norm(oracle.widen(out) - dense) / np.linalg.norm(dense):.4f}")
+
+
+def test_int8_head_groups_equal_one_launch_bitwise():
+    q, k, v = to_dev(*inputs.make_qkv(1500, 12, "frame", 71))
+    whole = fv.forward(q, k, v, mode="int8")
+    for g in (16, 8, 4):
+        assert torch.equal(whole, fv.forward_heads(q, k, v, g, mode="int8")), g
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")
@@ -419,3 +454,19 @@ def test_vsa_full_size(vsa72, tile):
     ref = oracle.vsa_attention(*(oracle.widen(t[heads]) for t in (q, k, v)), 1 / math.sqrt(128),
                                prefix, grid, tile, frac, rows=rows, idx=ref_idx)
     assert_close(oracle.widen(got), ref, f"vsa full size {tile}")
+
+
+@pytest.mark.timeout(400)
+def test_config4_int8(cfg4):
+    c = inputs.CONFIGS[4]
+    q, k, v = cfg4
+    out = fv.forward_heads(*to_dev(q, k, v), c.group, scale=c.scale, mode="int8")
+    rows = sample_rows(c.tokens, 24, 21)
+    heads = list(range(0, c.heads, 5)) + [c.heads - 1]
+    got = out[heads][:, rows].cpu()
+    qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
+    ref = oracle.int8_scores_attention(qw, kw, vw, c.scale, rows=rows)
+    assert_close(oracle.widen(got), ref, f"{c.name} int8")
+    dense = oracle.dense(qw, kw, vw, c.scale, rows=rows)
+    say(f"{c.name} int8: relative error against exact dense "
+        f"{np.linalg.norm(oracle.widen(got) - dense) / np.linalg.norm(dense):.4f}")

@@ -23,12 +23,14 @@ FVATTN_ERR_ALLOC = 3
 FVATTN_ERR_HIP = 4
 FVATTN_DENSE = 0
 FVATTN_BLOCK_SPARSE = 1
+FVATTN_DENSE_INT8QK = 2
 TILE = 128
 HEAD_DIM = 128
 MAX_TILES = 2048
 
-_MODES = {"dense": FVATTN_DENSE, "sparse": FVATTN_BLOCK_SPARSE,
-          FVATTN_DENSE: FVATTN_DENSE, FVATTN_BLOCK_SPARSE: FVATTN_BLOCK_SPARSE}
+_MODES = {"dense": FVATTN_DENSE, "sparse": FVATTN_BLOCK_SPARSE, "int8": FVATTN_DENSE_INT8QK,
+          FVATTN_DENSE: FVATTN_DENSE, FVATTN_BLOCK_SPARSE: FVATTN_BLOCK_SPARSE,
+          FVATTN_DENSE_INT8QK: FVATTN_DENSE_INT8QK}
 
 _lib = None
 
@@ -47,6 +49,7 @@ SIGNATURES = {
     "fvattn_forward_vsa": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _I, _I, _I, _I, _D, _P]),
     "fvattn_vsa_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _P, _P]),
     "fvattn_vsa_tile_count": (_I, [_I, _I, _I, _I, _I, _I]),
+    "fvattn_quantize_k": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "fvattn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -281,3 +284,14 @@ def vsa_select(q, k, prefix: int, grid, tile=(4, 4, 4), keep_frac: float = 0.1, 
                                         *(int(x) for x in grid), *(int(x) for x in tile),
                                         float(keep_frac), _ptr(out), _stream_ptr(stream)))
     return out
+
+
+def quantize_k(k, stream=None):
+    """fvattn_quantize_k: (codes int8 [heads, tokens, 128], scales float32 [heads, ceil(tokens/64)])."""
+    torch = _torch()
+    H, N, d = _check_qkv(k)
+    codes = torch.empty((H, N, d), dtype=torch.int8, device=k.device)
+    scales = torch.empty((H, -(-N // 64)), dtype=torch.float32, device=k.device)
+    with torch.cuda.device(k.device):
+        _check(load().fvattn_quantize_k(_ptr(k), H, N, d, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
+    return codes, scales

@@ -114,11 +114,36 @@ int run_selection(const uint16_t* q, const uint16_t* k, int heads, int tokens, i
   return hip_status(e);
 }
 
+// INT8 keys of one call: codes [H][N][128] int8 and block scales [H][ceil(N/64)].
+int forward_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int heads,
+                 int tokens, float scale, hipStream_t stream) {
+  const int nblk = (tokens + 63) / 64;
+  const size_t codeb = align256((size_t)heads * tokens * kHeadDim);
+  const size_t scaleb = align256(sizeof(float) * (size_t)heads * nblk);
+  void* base = nullptr;
+  if (test_fail_alloc() || hipMallocAsync(&base, codeb + scaleb, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  uint8_t* codes = (uint8_t*)base;
+  float* scales = (float*)((char*)base + codeb);
+  hipError_t e = fvattn::launch_quantize_k(k, codes, scales, heads, tokens, stream);
+  if (e == hipSuccess) {
+    fvattn::ListParams lp;
+    lp.kscale = scales;
+    e = fvattn::launch_attention_int8(q, codes, v, out, lp, heads, tokens, scale, stream);
+  }
+  const int rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(base, stream));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
 // Forward for one validated launch of `heads` heads.
 int forward_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int heads,
                 int tokens, float scale, int mode, double keep_frac, hipStream_t stream) {
   if (mode == FVATTN_DENSE)
     return hip_status(fvattn::launch_attention(q, k, v, out, nullptr, 0, heads, tokens, scale, stream));
+  if (mode == FVATTN_DENSE_INT8QK) return forward_int8(q, k, v, out, heads, tokens, scale, stream);
   const int T = tiles_of(tokens);
   const int keep = keep_of(T, keep_frac);
   SparseScratch s;
@@ -137,7 +162,8 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
                        int tokens, int head_dim, float scale, int mode, double keep_frac,
                        bool* empty) {
   *empty = false;
-  if (mode != FVATTN_DENSE && mode != FVATTN_BLOCK_SPARSE) return FVATTN_ERR_INVALID_ARG;
+  if (mode != FVATTN_DENSE && mode != FVATTN_BLOCK_SPARSE && mode != FVATTN_DENSE_INT8QK)
+    return FVATTN_ERR_INVALID_ARG;
   if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FVATTN_ERR_INVALID_ARG;
   if (mode == FVATTN_BLOCK_SPARSE && !keep_frac_ok(keep_frac)) return FVATTN_ERR_INVALID_ARG;
@@ -203,7 +229,7 @@ int fvattn_forward(const void* q, const void* k, const void* v, void* out, int h
   bool empty;
   int rc = check_forward_args(q, k, v, out, heads, tokens, head_dim, scale, mode, keep_frac, &empty);
   if (rc != FVATTN_OK || empty) return rc;
-  if (mode == FVATTN_BLOCK_SPARSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  if (mode != FVATTN_DENSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
   rc = check_device();
   if (rc != FVATTN_OK) return rc;
   return forward_one((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
@@ -257,7 +283,7 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
   if (rc != FVATTN_OK) return rc;
   if (group_heads != 16 && group_heads != 8 && group_heads != 4) return FVATTN_ERR_UNSUPPORTED;
   if (empty) return FVATTN_OK;
-  if (mode == FVATTN_BLOCK_SPARSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  if (mode != FVATTN_DENSE && test_fail_alloc()) return FVATTN_ERR_ALLOC;
   rc = check_device();
   if (rc != FVATTN_OK) return rc;
   const size_t per_head = (size_t)tokens * kHeadDim;
@@ -365,6 +391,19 @@ int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles,
   rc = hip_status(e);
   const int rf = hip_status(hipFreeAsync(kmT, st));
   return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
+                      float* scales_out, void* stream) {
+  if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if (heads == 0 || tokens == 0) return FVATTN_OK;
+  if (!k || !codes_out || !scales_out) return FVATTN_ERR_INVALID_ARG;
+  if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  return hip_status(fvattn::launch_quantize_k((const uint16_t*)k, (uint8_t*)codes_out, scales_out,
+                                              heads, tokens, (hipStream_t)stream));
 }
 
 int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int tile_h, int tile_w) {

@@ -61,6 +61,8 @@ namespace fvattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -83,6 +85,10 @@ constexpr int kWaitVm(int n) { return kWaitVmcnt0 | n; }
 __device__ __forceinline__ int k_swz(int row) {
   return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
 }
+// INT8 K rows (128 B): chunk swizzle; the 16 rows read by each 16-lane group of
+// an S^T operand load fall on 16 distinct 16-byte bank groups (row parity
+// selects the half of the 256-byte bank window, the swizzle the chunk).
+__device__ __forceinline__ int k8_swz(int row) { return ((row >> 1) & 3) | (((row >> 4) & 1) << 2); }
 // V rows: the 4 consecutive keys read by one 16-lane group of a transpose load
 // land on distinct chunk positions.
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
@@ -126,25 +132,35 @@ using Buf = std::integral_constant<int, B>;
 // kMode: 0 dense, 1 per-head kept-tile lists of `keep` tiles, 2 frame-window
 // lists shared by all heads (per-block counts, per-element frame mask), 3
 // VSA-H3 per-head lists of 64-key sub-tiles over the padded tile layout (Q
-// gathered from and O scattered to the packed token order).
+// gathered from and O scattered to the packed token order), 4 dense with INT8
+// query-key scores (K as int8 codes with per-64-key-block scales, Q quantized
+// per row here; S^T on v_mfma_i32_32x32x32_i8, PV unchanged in bf16).
 template <int kMode, int kWaves, int kStages, int kQB, int kBN>
 __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                                               const uint16_t* __restrict__ K,
                                               const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                               const int32_t* __restrict__ idx, int keep, int N,
                                               int qtiles, float c, ListParams wp) {
+  constexpr bool kI8 = kMode == 4;
+  constexpr bool kDenseWalk = kMode == 0 || kMode == 4;   // every key, no list
   constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
-  constexpr int kTileBytes = kBN * kRowBytes; // one K or V stage
+  constexpr int kTileBytes = kBN * kRowBytes; // one V (or bf16 K) stage
+  constexpr int kKRowBytes = kI8 ? kHeadDim : kRowBytes;      // K row in LDS: int8 or bf16
+  constexpr int kKTileBytes = kBN * kKRowBytes;
+  constexpr int kDK = kI8 ? 4 : 8;            // MFMAs along the head dimension
   constexpr int kBM = 32 * kQB * kWaves;
   constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
+  constexpr int kKLoadsPerWave = kKTileBytes / (1024 * kWaves);
+  static_assert(kKLoadsPerWave >= 1, "one wave-wide K load per wave at least");
+  static_assert(!kI8 || (kBN == 64 && kStages == 2), "INT8 scales are per 64-key stage, loaded one stage ahead");
   constexpr int kPrefetch = kStages - 1;
   static_assert(kMode != 1 || kBM == kTile, "per-head lists cover one selection tile");
   static_assert(kMode != 3 || (kBN == 64 && kBM == 256), "VSA entries are 64-key stages of 256-row blocks");
   // One LDS array per slot: distinct objects let the compiler see that a read
   // of one slot cannot alias a buffer-to-LDS load still landing in another,
   // so it does not wait for every load in flight before each LDS read.
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[kTileBytes], k_lds1[kTileBytes],
-      k_lds2[kStages > 2 ? kTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[kKTileBytes], k_lds1[kKTileBytes],
+      k_lds2[kStages > 2 ? kKTileBytes : 16];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[kTileBytes], v_lds1[kTileBytes],
       v_lds2[kStages > 2 ? kTileBytes : 16];
   unsigned char* const k_slots[3] = {k_lds0, k_lds1, k_lds2};
@@ -158,7 +174,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const size_t hoff = (size_t)h * (size_t)N * kHeadDim;
-  const uint16_t* Kh = K + hoff;
+  const unsigned char* Kh = (const unsigned char*)K + (size_t)h * N * kHeadDim * (kI8 ? 1 : 2);
   const uint16_t* Vh = V + hoff;
   // VSA: N counts padded slots; Q and O keep the packed token order
   const int qn = kMode == 3 ? wp.vsa.tokens : N;
@@ -168,7 +184,53 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   // qf[qb][dk][i] = Q[q0 + 32 qb + l32][16 dk + 8 g + i]; rows past N read as 0.
   const int q0 = qt * kBM + wave * 32 * kQB;
   bf16x8 qf[kQB][8];
-  if constexpr (kMode == 3) {
+  i32x4 qf8[kQB][4];   // INT8 mode: codes of Q^T, 16 dims per lane per 32-dim block
+  float crow[kQB];     // INT8 mode: scale * log2(e) * (this row's query scale)
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) crow[qb] = c;
+  if constexpr (kI8) {
+    // lane (row l32, half g) holds dims 32 dk + 16 g + 0..15 of its row; the
+    // row's scale is max |q| / 127 over both halves; rows past N read zeros
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      u32x4 w[8];
+      float m = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        w[x] = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, (32 * qb + l32) * kRowBytes + 64 * (x >> 1) + 32 * g + 16 * (x & 1), 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = w[x][e >> 1];
+          m = fmaxf(m, fabsf(__uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16))));
+        }
+      }
+      m = halfwave_max(m);
+      const float sq = m == 0.f ? 1.f : __fdiv_rn(m, 127.f);
+      crow[qb] = c * sq;
+#pragma unroll
+      for (int dk = 0; dk < 4; ++dk) {
+        i32x4 codes;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * wd + e;                       // dim 32 dk + 16 g + j
+            const uint32_t u = w[2 * dk + (j >> 3)][(j & 7) >> 1];
+            const float xv = __uint_as_float((j & 1) ? (u & 0xffff0000u) : (u << 16));
+            float qv = __builtin_rintf(__fdiv_rn(xv, sq));
+            qv = qv > 127.f ? 127.f : (qv < -127.f ? -127.f : qv);
+            word |= (uint32_t)((int)qv & 0xff) << (8 * e);
+          }
+          codes[wd] = (int)word;
+        }
+        qf8[qb][dk] = codes;
+      }
+    }
+  } else if constexpr (kMode == 3) {
     // gather: the lane's slot holds token vsa_slot_token(slot); padding reads
     // past the end of the descriptor and gets zeros
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, qn * kRowBytes);
@@ -200,7 +262,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                         : kMode == 2 ? idx + (size_t)qt * ktiles
                         : kMode == 3 ? idx + ((size_t)h * qtiles + qt) * (N / kBN)
                                      : nullptr;
-  const int nsub = kMode == 0   ? (N + kBN - 1) / kBN
+  const int nsub = kDenseWalk   ? (N + kBN - 1) / kBN
                    : kMode == 3 ? wp.counts[(size_t)h * qtiles + qt]
                                 : (kTile / kBN) * (kMode == 1 ? keep : wp.counts[qt]);
   // List entry of stage i (any i >= 0: past the end it repeats the last
@@ -214,36 +276,45 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     return irow[j < nlist ? j : nlist - 1];
   };
   auto kv_of = [&](int e, int i) -> int {
-    if (kMode == 0) return i * kBN;
+    if (kDenseWalk) return i * kBN;
     if (kMode == 3) return (e & 0xffff) * kBN | (e & kMaskFlag);
     const int flag = kMode == 2 ? (e & kMaskFlag) : 0;
     int t = kMode == 2 ? (e & ~kMaskFlag) : e;
     t = t < 0 ? 0 : (t >= ktiles ? ktiles - 1 : t);
     return (t * kTile + (i % kSub) * kBN) | flag;
   };
-  auto kv_start = [&](int i) -> int { return kv_of(kMode == 0 ? 0 : entry(i), i); };
+  auto kv_start = [&](int i) -> int { return kv_of(kDenseWalk ? 0 : entry(i), i); };
   // Raw entries of stages it+1 .. it+kStages, loaded one stage before use and
   // decoded only where used, so no stage waits on a scalar list load it has
   // just issued.
   int ring[kStages];
 #pragma unroll
-  for (int j = 0; j < kStages; ++j) ring[j] = kMode != 0 ? entry(1 + j) : 0;
+  for (int j = 0; j < kStages; ++j) ring[j] = !kDenseWalk ? entry(1 + j) : 0;
 
   // Buffer-to-LDS loads: wave-wide load i of this wave fills LDS rows
   // 4 (kLoadsPerWave wave + i) + (lane >> 4), 16-byte slot lane & 15; the lane
   // fetches the global chunk that the swizzle places in that slot.
-  int koffg[kLoadsPerWave], voffg[kLoadsPerWave];
+  int koffg[kKLoadsPerWave], voffg[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kKLoadsPerWave; ++i) {
+    if constexpr (kI8) {   // 8 rows of 128 B per wave-wide load
+      const int row = 8 * (kKLoadsPerWave * wave + i) + (lane >> 3), slot = lane & 7;
+      koffg[i] = row * kKRowBytes + ((slot ^ k8_swz(row)) << 4);
+    } else {
+      const int row = 4 * (kKLoadsPerWave * wave + i) + (lane >> 4), slot = lane & 15;
+      koffg[i] = row * kKRowBytes + ((slot ^ k_swz(row)) << 4);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     const int row = 4 * (kLoadsPerWave * wave + i) + (lane >> 4), slot = lane & 15;
-    koffg[i] = row * kRowBytes + ((slot ^ k_swz(row)) << 4);
     voffg[i] = row * kRowBytes + ((slot ^ v_swz(row)) << 4);
   }
   auto load_k = [&](int kv0, auto bufc) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
-    unsigned char* dst = k_slots[decltype(bufc)::value] + wave * kLoadsPerWave * 1024;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kKRowBytes, (N - kv0) * kKRowBytes);
+    unsigned char* dst = k_slots[decltype(bufc)::value] + wave * kKLoadsPerWave * 1024;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i)
+    for (int i = 0; i < kKLoadsPerWave; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, koffg[i], 0, 0, 0);
   };
   auto load_v = [&](int kv0, auto bufc) {
@@ -256,11 +327,12 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 
   // S^T operand: row key_of_row(l32) (+32 for the second 32-key block), chunk
   // 2 dk + g; byte offsets within a stage, one per dk.
-  int koff[8];
+  int koff[kDK];
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk) koff[dk] = krow * kRowBytes + (((2 * dk + g) ^ k_swz(krow)) << 4);
+    for (int dk = 0; dk < kDK; ++dk)
+      koff[dk] = krow * kKRowBytes + (((2 * dk + g) ^ (kI8 ? k8_swz(krow) : k_swz(krow))) << 4);
   }
   // V^T operand by transpose load: 16-lane group G = lane >> 4 covers head
   // dims 32 db + 16 (G & 1) + 0..15 and keys 32 kb + 16 (G >> 1) + 8 s + 0..7;
@@ -305,14 +377,34 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[qb][kb][r] = 0.f;
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk)
+    for (int dk = 0; dk < kDK; ++dk)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
-        const bf16x8 a = *(const bf16x8*)(kb0 + koff[dk] + kb * 32 * kRowBytes);
+        if constexpr (kI8) {
+          // int32 scores in the float registers (bit patterns); converted after
+          const i32x4 a = *(const i32x4*)(kb0 + koff[dk] + kb * 32 * kKRowBytes);
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][dk], S[qb][kb], 0, 0, 0);
+          for (int qb = 0; qb < kQB; ++qb)
+            S[qb][kb] = __builtin_bit_cast(
+                f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            a, qf8[qb][dk], __builtin_bit_cast(i32x16, S[qb][kb]), 0, 0, 0));
+        } else {
+          const bf16x8 a = *(const bf16x8*)(kb0 + koff[dk] + kb * 32 * kKRowBytes);
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+            S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][dk], S[qb][kb], 0, 0, 0);
+        }
       }
+  };
+  // INT8 mode: the exact int32 scores to float (|S| < 2^24, exact).  The
+  // whole accumulator is reinterpreted at once: a bit cast of one vector
+  // element does not read that element.
+  auto to_float = [&](f32x16 (&S)[kQB][kKB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+        S[qb][kb] = __builtin_convertvector(__builtin_bit_cast(i32x16, S[qb][kb]), f32x16);
   };
   // Keys past N: -inf scores.  Only stages that reach past the end need it.
   auto mask = [&](f32x16 (&S)[kQB][kKB], int kv0) {
@@ -392,7 +484,9 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
         }
   };
   // Row max of a stage, in scaled log2 units.
-  auto rowmax = [&](const f32x16 (&S)[kQB][kKB], float (&mx)[kQB]) {
+  // cm[qb]: the multiplier of this stage's scores (c, or in INT8 mode
+  // crow * the stage's key scale).
+  auto rowmax = [&](const f32x16 (&S)[kQB][kKB], float (&mx)[kQB], const float (&cm)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       float m = S[qb][0][0];
@@ -400,7 +494,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, S[qb][kb][r]);
-      mx[qb] = halfwave_max(m) * c;
+      mx[qb] = halfwave_max(m) * cm[qb];
     }
   };
   // Raise the running max (and rescale O and the sums) when some row of the
@@ -425,7 +519,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   };
   // P = exp2(S c - m) as bf16 B-operands; P[qb][st] covers keys 32 kb + 16 g + 8 s + 0..7
   // with st = 2 kb + s.
-  auto softmax = [&](const f32x16 (&S)[kQB][kKB], bf16x8 (&P)[kQB][2 * kKB]) {
+  auto softmax = [&](const f32x16 (&S)[kQB][kKB], bf16x8 (&P)[kQB][2 * kKB], const float (&cm)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       float ps[2] = {0.f, 0.f};
@@ -433,7 +527,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[qb][kb][r], c, -m_run[qb]));
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[qb][kb][r], cm[qb], -m_run[qb]));
           ps[r & 1] += p;
           P[qb][2 * kb + (r >> 3)][r & 7] = (__bf16)p;
         }
@@ -472,7 +566,20 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   // stage it+1.  On the last stage the S^T product reads a stale slot and its
   // result is discarded.
   auto loads_at = [&](int i) {   // wave-wide loads a stage issues (uniform)
-    return (i + kStages < nsub ? kLoadsPerWave : 0) + (i + kPrefetch < nsub ? kLoadsPerWave : 0);
+    return (i + kStages < nsub ? kKLoadsPerWave : 0) + (i + kPrefetch < nsub ? kLoadsPerWave : 0);
+  };
+  // INT8 mode: key scales of stages it (sk_cur), it+1 (sk_next) and it+2
+  // (loaded during stage it with a vector load, so the stage-top vmcnt wait
+  // covers it).  Other modes: the multiplier is c throughout.
+  const __amdgpu_buffer_rsrc_t rks =
+      make_rsrc(kI8 ? wp.kscale + (size_t)h * nsub : nullptr, kI8 ? nsub * 4 : 0);
+  auto key_scale = [&](int i) -> float {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4 * i, 0, 0));
+  };
+  float sk_cur = 1.f, sk_next = 1.f;
+  auto multipliers = [&](float sk, float (&cm)[kQB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) cm[qb] = kI8 ? crow[qb] * sk : c;
   };
   auto stage = [&](auto kc, int it, f32x16 (&Scur)[kQB][kKB], f32x16 (&Snext)[kQB][kKB]) {
     constexpr int k = decltype(kc)::value;
@@ -496,15 +603,19 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     if (it + kStages < nsub) load_k(kv_of(ring[kStages - 1], it + kStages) & ~kMaskFlag, Buf<k % kStages>());
     if (it + kPrefetch < nsub)
       load_v(kv_of(ring[kPrefetch - 1], it + kPrefetch) & ~kMaskFlag, Buf<(k + kStages - 1) % kStages>());
-    const int ahead = kMode != 0 ? entry(it + 1 + kStages) : 0;
+    const int ahead = !kDenseWalk ? entry(it + 1 + kStages) : 0;
+    const float sk_ahead = kI8 ? key_scale(it + 2) : 1.f;
+    float cm_cur[kQB], cm_next[kQB];
+    multipliers(sk_cur, cm_cur);
+    multipliers(sk_next, cm_next);
 
-    softmax(Scur, P);
+    softmax(Scur, P, cm_cur);
     qk(Buf<kSlotK>(), Snext);
     // Region 1: one K-operand read per (dk, kb) feeds kQB MFMAs; the softmax's
     // ~56 kQB kKB VALU instructions are spread between the MFMAs.  Reads run
     // one operand ahead.
     {
-      constexpr int kOps = 8 * kKB, kValuPerMfma = (56 * kKB * kQB + kOps * kQB - 1) / (kOps * kQB);
+      constexpr int kOps = kDK * kKB, kValuPerMfma = (56 * kKB * kQB + kOps * kQB - 1) / (kOps * kQB);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
@@ -517,6 +628,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
       }
     }
 
+    if constexpr (kI8) to_float(Snext);
     if constexpr (kMode == 2) {
       if (has_next && (kv_next & kMaskFlag)) window_mask(Snext, kv_next & ~kMaskFlag);
     } else if constexpr (kMode == 3) {
@@ -530,11 +642,12 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     // other wave on the SIMD is in its softmax, the matrix pipe stays fed.
     __builtin_amdgcn_s_setprio(1);
     pv(Buf<kSlotV>(), P);
-    rowmax(Snext, mx);
+    rowmax(Snext, mx, cm_next);
     // Region 2: two transpose reads per (db, st) V operand feed kQB MFMAs; the
-    // row max of the next stage fills the gaps.  Reads run one operand ahead.
+    // row max of the next stage (and in INT8 mode the conversion of its
+    // scores) fills the gaps.  Reads run one operand ahead.
     {
-      constexpr int kOps = 4 * 2 * kKB;
+      constexpr int kOps = 4 * 2 * kKB, kValu = kI8 ? 4 : 2;
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
@@ -542,18 +655,20 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, kValu, 1);
         }
       }
     }
 
     __builtin_amdgcn_s_setprio(0);
     if (has_next) maybe_rescale(mx);
-    if constexpr (kMode != 0) {
+    if constexpr (!kDenseWalk) {
 #pragma unroll
       for (int j = 0; j + 1 < kStages; ++j) ring[j] = ring[j + 1];
       ring[kStages - 1] = ahead;
     }
+    sk_cur = sk_next;
+    sk_next = sk_ahead;
   };
 
   // prologue: K(0..kStages-1) and V(0..kStages-2) started, scores and max of stage 0
@@ -565,17 +680,23 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     if (kStages > 2 && 2 < nsub) load_k(kv_of(ring[1], 2) & ~kMaskFlag, Buf<2 % kStages>());
     load_v(kv0, Buf<0>());
     if (kStages > 2 && 1 < nsub) load_v(kv1, Buf<1 % kStages>());
+    if constexpr (kI8) {
+      sk_cur = key_scale(0);
+      sk_next = key_scale(1);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm(0));
     __builtin_amdgcn_s_barrier();
     qk(Buf<0>(), SA);
+    if constexpr (kI8) to_float(SA);
     if constexpr (kMode == 2) {
       if (kv0e & kMaskFlag) window_mask(SA, kv0);
     } else if constexpr (kMode == 3) {
       if (kv0e & kMaskFlag) vsa_mask(SA, entry(0));
     }
     else if (kv0 + kBN > N) mask(SA, kv0);
-    float mx[kQB];
-    rowmax(SA, mx);
+    float mx[kQB], cm0[kQB];
+    multipliers(sk_cur, cm0);
+    rowmax(SA, mx, cm0);
     maybe_rescale(mx);
   }
   // Unrolled so that every slot and score register set is a constant.
@@ -663,6 +784,19 @@ hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const u
   if (blocks <= 0) return hipSuccess;
   attn_fwd_kernel<2, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
       q, k, v, out, idx, 0, tokens, qtiles, c, wp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
+                                 uint16_t* out, const ListParams& lp, int heads, int tokens,
+                                 float scale, hipStream_t stream) {
+  // the dense shape: 256 query rows per workgroup (8 waves), 64-key stages
+  const float c = scale * 1.4426950408889634f;  // scale * log2(e)
+  const int qtiles = (tokens + 255) / 256;
+  const long long blocks = (long long)heads * qtiles;
+  if (blocks <= 0) return hipSuccess;
+  attn_fwd_kernel<4, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+      q, (const uint16_t*)kq, v, out, nullptr, 0, tokens, qtiles, c, lp);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ struct ListParams {
   // and starting with them keeps them out of the tail of the launch
   int first_block = 0;
   VsaGeom vsa;
+  // INT8 query-key mode: per-64-key-block key scales [heads][ceil(N / 64)]
+  const float* kscale = nullptr;
 };
 
 // Dense (idx == nullptr) or tile-list (idx != nullptr, `keep` entries per query
@@ -137,6 +139,17 @@ hipError_t launch_vsa_lists(const int32_t* idx, int keep, const VsaGeom& g, int 
 hipError_t launch_attention_vsa(const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
                                 uint16_t* out, const int32_t* lists, const ListParams& lp,
                                 int heads, float scale, hipStream_t stream);
+
+// INT8 keys: codes [heads][tokens][128] int8 and per-64-key-block scales
+// [heads][ceil(tokens / 64)] float.
+hipError_t launch_quantize_k(const uint16_t* k, uint8_t* codes, float* scales, int heads,
+                             int tokens, hipStream_t stream);
+
+// Dense attention with INT8 query-key scores: kq = codes from launch_quantize_k
+// (lp.kscale = their scales); queries are quantized per row in the kernel.
+hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
+                                 uint16_t* out, const ListParams& lp, int heads, int tokens,
+                                 float scale, hipStream_t stream);
 
 // S1: fp64 tile means.  transposed == false: out [heads][T][128];
 // transposed == true: out [heads][128][T].
