@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
+PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_dense_72576x56_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "video_diffusion_transformer_amd", "csrc", "attn_fwd.hip")
 
@@ -130,7 +131,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8"], default=None,
+    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8", "vda"], default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
                          "0 for window and vsa, which are timed outside the step)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -184,6 +185,7 @@ def main():
     do_window = args.only in (None, "window")
     do_vsa = args.only in (None, "vsa")
     do_int8 = args.only in (None, "int8")
+    do_vda = args.only in (None, "vda")
     if not do_dense:
         flop_dense = 0.0
     if not do_sparse:
@@ -314,6 +316,33 @@ def main():
                "tflops_effective": round(flop_v / (vm * 1e-3) / 1e12, 2),
                "density": round(flop_v / (4.0 * ntok * ntok * 128 * HEADS), 4)}
 
+    # Video Delta Attention (the linear branch of Video DeltaNet), outside the
+    # step: 72 latent frames of 1,008 tokens, 56 heads, 5-frame chunks +-1
+    vda = None
+    if do_vda:
+        torch.cuda.empty_cache()
+        frames = TOKENS // FRAME_TOKENS
+        log("generating Video Delta Attention inputs", frames, "frames x", HEADS, "heads")
+        vin = [t.to(dev) for t in inputs.make_vda_inputs(frames, HEADS, SEED, FRAME_TOKENS)]
+        vout = torch.empty((HEADS, TOKENS, 128), dtype=torch.float32, device=dev)
+        a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        a_ms = []
+        for i in range(4):
+            a_ev[0].record(stream)
+            fv.vda_forward(*vin, FRAME_TOKENS, 5, 1, out=vout)
+            a_ev[1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                a_ms.append(a_ev[0].elapsed_time(a_ev[1]))
+        del vin, vout
+        am = float(np.median(a_ms))
+        d2 = 128.0 * 128.0
+        flop_a = (4.0 * TOKENS * d2 + 2.0 * TOKENS * d2) * HEADS \
+            + (2.0 + 2.0) * 128.0 * d2 * frames * HEADS + 2 * 2.0 * 128.0 * d2 * (frames - 2) * HEADS
+        vda = {"ms": round(am, 3), "flop": flop_a, "tflops": round(flop_a / (am * 1e-3) / 1e12, 2),
+               "frac_peak_fp32_mfma": round(flop_a / (am * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+               "frames": frames, "frame_tokens": FRAME_TOKENS}
+
     d_ms = float(np.median(dense_ms))
     s_ms = float(np.median(sparse_ms))
     dense_tflops = flop_dense / max(d_ms * 1e-3, 1e-12) / 1e12
@@ -368,6 +397,8 @@ def main():
         result["window"] = window
     if vsa is not None:
         result["vsa"] = vsa
+    if vda is not None:
+        result["vda"] = vda
     if int8 is not None:
         if do_dense:
             int8["speedup_vs_dense"] = round(d_ms / int8["ms"], 3)

@@ -208,6 +208,40 @@ int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int til
 int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
                       float* scales_out, void* stream);
 
+/* Video Delta Attention, the linear branch of Video DeltaNet (FreeVideo page,
+ * section "Where Video DeltaNet comes in"), before its learned gate, norm and
+ * projection.  Per head, latent frame t (tokens [t*frame_tokens,
+ * (t+1)*frame_tokens)) writes the state S (d_v x d_k = 128 x 128) as
+ *   S_t = (S_prev Diag(alpha_t) + B_t)(I + A_t)^-1,
+ *   A_t = sum_u beta_u k_u k_u^T, B_t = sum_u beta_u v_u k_u^T,
+ * the closed-form minimizer of 1/2||S - S_prev Diag(alpha_t)||^2 +
+ * 1/2 sum_u beta_u ||S k_u - v_u||^2.  A forward scan writes frames 1..F-2 in
+ * order and a reverse scan F-2..1, both from S_text / 2 (the first and last
+ * frames are the softmax anchors and are never written).  A query of frame f,
+ * chunk c = f / chunk_frames, reads out = fwd[lo] q + rev[hi] q with
+ * lo = clamp((c - neighbours) * chunk_frames, 0, F) and hi = clamp((c +
+ * neighbours + 1) * chunk_frames, 0, F) (the frames before and after its
+ * softmax window, see fvattn_forward_window); a query of an anchor frame reads
+ * fwd[0] q + rev[F] q = S_text q.
+ * q, k, v: bf16 [heads][frames * frame_tokens][128]; beta: float
+ * [heads][frames * frame_tokens]; alpha: float [heads][frames][128]; s_text:
+ * float [heads][128][128] (row = value dim); out: float
+ * [heads][frames * frame_tokens][128].  All device pointers.  Products and
+ * the inverse run in fp32 (matrix cores, Gauss-Jordan without pivoting on the
+ * symmetric I + A_t, eigenvalues >= 1 for beta >= 0).  Uses stream-ordered
+ * scratch of (5 * heads * frames + 2 * heads * (frames + 1)) * 64 KiB. */
+int fvattn_vda_forward(const void* q, const void* k, const void* v, const float* beta,
+                       const float* alpha, const float* s_text, float* out, int heads, int frames,
+                       int frame_tokens, int head_dim, int chunk_frames, int neighbours,
+                       void* stream);
+
+/* The two scans of fvattn_vda_forward alone: fwd_out, rev_out float
+ * [heads][frames + 1][128][128]; fwd[t] has absorbed the written frames
+ * before t, rev[t] those from t on; fwd[0] = rev[frames] = s_text / 2. */
+int fvattn_vda_states(const void* k, const void* v, const float* beta, const float* alpha,
+                      const float* s_text, int heads, int frames, int frame_tokens, int head_dim,
+                      float* fwd_out, float* rev_out, void* stream);
+
 /* Step S1 alone, for checking: fp64 tile means of x, bf16 [heads][tokens][128]
  * in, means_out fp64 [heads][T][128] out (device pointers). */
 int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double* means_out,

@@ -285,3 +285,26 @@ def test_int8_mode_argument_checks(lib, monkeypatch):
     assert _fwd(lib, mode=2) == fv.FVATTN_ERR_ALLOC
     assert lib.fvattn_forward_heads(BOGUS, BOGUS, BOGUS, BOGUS, 56, 16, 1008, 128, 0.088, 2, 0.1,
                                     NULL) == fv.FVATTN_ERR_ALLOC
+
+
+def test_vda_argument_checks(lib, monkeypatch):
+    fw, st = lib.fvattn_vda_forward, lib.fvattn_vda_states
+    args = lambda **kw: [kw.get(n, d) for n, d in [("q", BOGUS), ("k", BOGUS), ("v", BOGUS), ("b", BOGUS),
+                                                  ("a", BOGUS), ("s", BOGUS), ("o", BOGUS), ("h", 2),
+                                                  ("f", 7), ("ft", 64), ("hd", 128), ("ch", 5), ("nb", 1)]]
+    assert fw(*args(q=NULL), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(o=NULL), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(b=NULL), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(h=-1), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(ch=0), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(nb=-1), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(ft=0), NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert fw(*args(hd=64), NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert fw(*args(q=NULL, k=NULL, v=NULL, h=0), NULL) == fv.FVATTN_OK
+    assert fw(*args(q=NULL, k=NULL, v=NULL, f=0), NULL) == fv.FVATTN_OK
+    assert st(BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, 2, 7, 64, 128, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert st(BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, 2, 7, 64, 96, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert st(NULL, NULL, NULL, NULL, NULL, 0, 7, 64, 128, NULL, NULL, NULL) == fv.FVATTN_OK
+    monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
+    assert fw(*args(), NULL) == fv.FVATTN_ERR_ALLOC
+    assert st(BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, 2, 7, 64, 128, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_ALLOC

@@ -344,6 +344,49 @@ def test_int8_head_groups_equal_one_launch_bitwise():
         assert torch.equal(whole, fv.forward_heads(q, k, v, g, mode="int8")), g
 
 
+# ------------------------------------------------------------------ Video Delta Attention
+
+def _vda_case(frames, ft, heads, seed):
+    q, k, v, beta, alpha, s_text = inputs.make_vda_inputs(frames, heads, seed, frame_tokens=ft)
+    dev = to_dev(q, k, v, beta, alpha, s_text)
+    wide = [oracle.widen(t) for t in (q, k, v)] + [t.double().numpy() for t in (beta, alpha, s_text)]
+    return dev, wide
+
+
+# The Video Delta Attention path runs in fp32 (unit roundoff 6e-8): sums of up
+# to 1,008 products, a 128-step elimination and up to 70 chained state
+# products, against the fp64 oracle.  The contraction of the carried state keeps
+# errors from growing along the scan; 2e-5 relative (about 300 roundoffs) is
+# the bar, the measured error is ~1e-6.
+def assert_close_rel(got, ref, what, rel_max=2e-5):
+    got = np.asarray(got, dtype=np.float64)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = float(np.abs(got - ref).max()) / scale
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    say(f"{what}: max_abs/max|ref|={err:.3e} rel_fro={rel:.3e} max|ref|={scale:.3e}")
+    assert err <= rel_max and rel <= rel_max, (what, err, rel)
+
+
+@pytest.mark.parametrize("frames,ft", [(1, 5), (2, 64), (3, 64), (7, 100), (12, 1008)])
+def test_vda_states_match_oracle(frames, ft):
+    say("vda states", frames, ft)
+    (q, k, v, beta, alpha, s_text), wide = _vda_case(frames, ft, 2, 900 + frames)
+    fwd, rev = fv.vda_states(k, v, beta, alpha, s_text, ft)
+    for h in range(2):
+        rf, rr = oracle.scan_states(wide[1][h], wide[2][h], wide[3][h], wide[4][h], wide[5][h], ft)
+        assert_close_rel(fwd[h].cpu().numpy(), rf, f"vda fwd states F={frames} ft={ft} h={h}")
+        assert_close_rel(rev[h].cpu().numpy(), rr, f"vda rev states F={frames} ft={ft} h={h}")
+
+
+@pytest.mark.parametrize("frames,ft,chunk,nb", [(7, 64, 2, 1), (12, 100, 3, 1), (20, 64, 5, 1), (9, 130, 3, 0)])
+def test_vda_readout_matches_oracle(frames, ft, chunk, nb):
+    say("vda readout", frames, ft, chunk, nb)
+    (q, k, v, beta, alpha, s_text), wide = _vda_case(frames, ft, 2, 950 + frames)
+    out = fv.vda_forward(q, k, v, beta, alpha, s_text, ft, chunk, nb).cpu().numpy()
+    ref = oracle.vda_attention(*wide, ft, chunk, nb)
+    assert_close_rel(out, ref, f"vda readout F={frames} ft={ft} chunk={chunk} nb={nb}")
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.fixture(scope="module")
@@ -470,3 +513,13 @@ def test_config4_int8(cfg4):
     dense = oracle.dense(qw, kw, vw, c.scale, rows=rows)
     say(f"{c.name} int8: relative error against exact dense "
         f"{np.linalg.norm(oracle.widen(got) - dense) / np.linalg.norm(dense):.4f}")
+
+
+@pytest.mark.timeout(400)
+def test_vda_full_size():
+    frames, ft = 72, 1008
+    say("vda full size", frames, ft)
+    (q, k, v, beta, alpha, s_text), wide = _vda_case(frames, ft, 2, 77)
+    out = fv.vda_forward(q, k, v, beta, alpha, s_text, ft, 5, 1).cpu().numpy()
+    ref = oracle.vda_attention(*wide, ft, 5, 1)
+    assert_close_rel(out, ref, "vda 72 x 1008 readout")

@@ -50,6 +50,8 @@ SIGNATURES = {
     "fvattn_vsa_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _P, _P]),
     "fvattn_vsa_tile_count": (_I, [_I, _I, _I, _I, _I, _I]),
     "fvattn_quantize_k": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "fvattn_vda_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fvattn_vda_states": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "fvattn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -295,3 +297,47 @@ def quantize_k(k, stream=None):
     with torch.cuda.device(k.device):
         _check(load().fvattn_quantize_k(_ptr(k), H, N, d, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
     return codes, scales
+
+
+def _check_f32(*ts):
+    torch = _torch()
+    for t in ts:
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous float32 device tensors")
+
+
+def vda_forward(q, k, v, beta, alpha, s_text, frame_tokens: int, chunk_frames: int = 5,
+                neighbours: int = 1, out=None, stream=None):
+    """fvattn_vda_forward: Video Delta Attention readout, float32 [heads, tokens, 128]."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    F = N // int(frame_tokens)
+    if F * int(frame_tokens) != N:
+        raise ValueError("tokens must be frames * frame_tokens")
+    _check_f32(beta, alpha, s_text)
+    if tuple(beta.shape) != (H, N) or tuple(alpha.shape) != (H, F, d) or tuple(s_text.shape) != (H, d, d):
+        raise ValueError("beta [H, N], alpha [H, F, 128], s_text [H, 128, 128] expected")
+    if out is None:
+        out = torch.empty((H, N, d), dtype=torch.float32, device=q.device)
+    _check_f32(out)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_vda_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                         _ptr(s_text), _ptr(out), H, F, int(frame_tokens), d,
+                                         int(chunk_frames), int(neighbours), _stream_ptr(stream)))
+    return out
+
+
+def vda_states(k, v, beta, alpha, s_text, frame_tokens: int, stream=None):
+    """fvattn_vda_states: (fwd, rev) float32 [heads, frames + 1, 128, 128]."""
+    torch = _torch()
+    H, N, d = _check_qkv(k, v)
+    F = N // int(frame_tokens)
+    if F * int(frame_tokens) != N:
+        raise ValueError("tokens must be frames * frame_tokens")
+    _check_f32(beta, alpha, s_text)
+    fwd = torch.empty((H, F + 1, d, d), dtype=torch.float32, device=k.device)
+    rev = torch.empty_like(fwd)
+    with torch.cuda.device(k.device):
+        _check(load().fvattn_vda_states(_ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(s_text), H, F,
+                                        int(frame_tokens), d, _ptr(fwd), _ptr(rev), _stream_ptr(stream)))
+    return fwd, rev

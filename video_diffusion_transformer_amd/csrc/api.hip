@@ -215,6 +215,16 @@ int check_vsa_args(int heads, int tokens, int head_dim, int prefix, int frames, 
   return FVATTN_OK;
 }
 
+// Checks shared by the Video Delta Attention entry points.
+int check_vda_args(int heads, int frames, int frame_tokens, int head_dim) {
+  if (heads < 0 || frames < 0 || frame_tokens < 0) return FVATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  if ((long long)frames * frame_tokens * kHeadDim > kMaxPerHead ||
+      (long long)(frames + 1) * kHeadDim * kHeadDim > kMaxPerHead)
+    return FVATTN_ERR_UNSUPPORTED;
+  return FVATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,6 +414,65 @@ int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t
   if (rc != FVATTN_OK) return rc;
   return hip_status(fvattn::launch_quantize_k((const uint16_t*)k, (uint8_t*)codes_out, scales_out,
                                               heads, tokens, (hipStream_t)stream));
+}
+
+int fvattn_vda_states(const void* k, const void* v, const float* beta, const float* alpha,
+                      const float* s_text, int heads, int frames, int frame_tokens, int head_dim,
+                      float* fwd_out, float* rev_out, void* stream) {
+  int rc = check_vda_args(heads, frames, frame_tokens, head_dim);
+  if (rc != FVATTN_OK) return rc;
+  if (heads == 0 || frames == 0) return FVATTN_OK;
+  if (frame_tokens == 0) return FVATTN_ERR_INVALID_ARG;
+  if (!k || !v || !beta || !alpha || !s_text || !fwd_out || !rev_out) return FVATTN_ERR_INVALID_ARG;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  void* scratch = nullptr;
+  const size_t bytes = sizeof(float) * 5 * (size_t)heads * frames * kHeadDim * kHeadDim;
+  if (hipMallocAsync(&scratch, bytes, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  rc = hip_status(fvattn::launch_vda_states((const uint16_t*)k, (const uint16_t*)v, beta, alpha,
+                                            s_text, heads, frames, frame_tokens, (float*)scratch,
+                                            fwd_out, rev_out, st));
+  const int rf = hip_status(hipFreeAsync(scratch, st));
+  return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_vda_forward(const void* q, const void* k, const void* v, const float* beta,
+                       const float* alpha, const float* s_text, float* out, int heads, int frames,
+                       int frame_tokens, int head_dim, int chunk_frames, int neighbours,
+                       void* stream) {
+  int rc = check_vda_args(heads, frames, frame_tokens, head_dim);
+  if (rc != FVATTN_OK) return rc;
+  if (chunk_frames < 1 || neighbours < 0) return FVATTN_ERR_INVALID_ARG;
+  if (heads == 0 || frames == 0) return FVATTN_OK;
+  if (frame_tokens == 0) return FVATTN_ERR_INVALID_ARG;
+  if (!q || !k || !v || !beta || !alpha || !s_text || !out) return FVATTN_ERR_INVALID_ARG;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t mat = (size_t)kHeadDim * kHeadDim;
+  const size_t work = 5 * (size_t)heads * frames * mat, states = (size_t)heads * (frames + 1) * mat;
+  void* scratch = nullptr;
+  if (hipMallocAsync(&scratch, sizeof(float) * (work + 2 * states), st) != hipSuccess) {
+    (void)hipGetLastError();
+    return FVATTN_ERR_ALLOC;
+  }
+  float* w = (float*)scratch;
+  float* fwd = w + work;
+  float* rev = fwd + states;
+  hipError_t e = fvattn::launch_vda_states((const uint16_t*)k, (const uint16_t*)v, beta, alpha,
+                                           s_text, heads, frames, frame_tokens, w, fwd, rev, st);
+  if (e == hipSuccess)
+    e = fvattn::launch_vda_readout((const uint16_t*)q, fwd, rev, heads, frames, frame_tokens,
+                                   chunk_frames, neighbours, out, st);
+  rc = hip_status(e);
+  const int rf = hip_status(hipFreeAsync(scratch, st));
+  return rc != FVATTN_OK ? rc : rf;
 }
 
 int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int tile_h, int tile_w) {

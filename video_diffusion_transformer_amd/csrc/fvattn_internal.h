@@ -151,6 +151,19 @@ hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uin
                                  uint16_t* out, const ListParams& lp, int heads, int tokens,
                                  float scale, hipStream_t stream);
 
+// Video Delta Attention: forward and reverse states [heads][frames + 1][128][128]
+// (fp32) from k, v (bf16 [heads][frames * ft][128]), beta [heads][frames * ft],
+// alpha [heads][frames][128] and s_text [heads][128][128]; scratch holds
+// 5 * heads * frames * 128 * 128 floats.
+hipError_t launch_vda_states(const uint16_t* k, const uint16_t* v, const float* beta,
+                             const float* alpha, const float* s_text, int heads, int frames,
+                             int ft, float* scratch, float* fwd, float* rev, hipStream_t stream);
+
+// Video Delta Attention readout: out (fp32 [heads][frames * ft][128]) =
+// (fwd[lo] + rev[hi]) q per query of each frame.
+hipError_t launch_vda_readout(const uint16_t* q, const float* fwd, const float* rev, int heads,
+                              int frames, int ft, int chunk, int nb, float* out, hipStream_t stream);
+
 // S1: fp64 tile means.  transposed == false: out [heads][T][128];
 // transposed == true: out [heads][128][T].
 hipError_t launch_tile_means(const uint16_t* x, double* out, int heads, int tokens,

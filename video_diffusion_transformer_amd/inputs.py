@@ -142,3 +142,24 @@ def make_packed_qkv(prefix: int, grid, heads: int, seed: int):
         return vq, vk, vv
     pq, pk, pv = make_qkv(prefix, heads, "iid", seed + 1000)
     return tuple(torch.cat([a, b], dim=1).contiguous() for a, b in ((pq, vq), (pk, vk), (pv, vv)))
+
+
+
+def make_vda_inputs(frames: int, heads: int, seed: int, frame_tokens: int = TOKENS_PER_LATENT_FRAME):
+    """Inputs of the Video Delta Attention branch (synthetic; the pages give no
+    activations): q, k unit-length directions (normalized N(0, I) draws, as the
+    branch L2-normalizes them) and v N(0, 1), all bf16 [heads][frames *
+    frame_tokens][128]; beta U(0.05, 0.95) per token, alpha U(0.8, 1.0) per
+    frame and key dim, s_text 0.1 N(0, 1) [heads][128][128], all float32."""
+    N = frames * frame_tokens
+    rq, rk, rv, rs = (_rng(seed, t) for t in (_TAG_Q, _TAG_K, _TAG_V, _TAG_SHARED))
+    out = []
+    for r, unit in ((rq, True), (rk, True), (rv, False)):
+        x = r.standard_normal((heads, N, HEAD_DIM), dtype=np.float32)
+        if unit:
+            x = x / np.linalg.norm(x, axis=2, keepdims=True)
+        out.append(_to_bf16(x))
+    beta = torch.from_numpy(rs.uniform(0.05, 0.95, (heads, N)).astype(np.float32))
+    alpha = torch.from_numpy(rs.uniform(0.8, 1.0, (heads, frames, HEAD_DIM)).astype(np.float32))
+    s_text = torch.from_numpy((0.1 * rs.standard_normal((heads, HEAD_DIM, HEAD_DIM))).astype(np.float32))
+    return (*out, beta, alpha, s_text)
