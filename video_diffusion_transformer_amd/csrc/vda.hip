@@ -28,6 +28,7 @@ namespace fvattn {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = kHeadDim;           // 128
 constexpr int kMat = kD * kD;          // one state-sized matrix
@@ -93,54 +94,123 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
   store_row_tile(B + off, w, acc_b, lane);
 }
 
-// M_t = (I + A_t)^-1 by Gauss-Jordan in place, and P_t = Diag(alpha_t) M_t.
-// Thread (column j, parity p) keeps rows p, p + 2, ... of column j in
-// registers.  Step k needs column k (published by its two owners) and row k
-// (published by the owners of row k in every column) through LDS, double
-// buffered by step parity so that one barrier per step suffices: a buffer is
-// rewritten two steps later, after every thread has passed another barrier.
+// M_t = (I + A_t)^-1 by blocked Gauss-Jordan in place, and P_t = Diag(alpha_t)
+// M_t.  Four steps over 32-column blocks b: D = a[b][b] is inverted by one wave
+// (unblocked elimination of the 32 x 32 block), then, as 32 x 32 tile products
+// on the matrix cores (k = 32):
+//   row block       a[b][j] = D^-1 a[b][j]                  (j != b)
+//   trailing blocks a[i][j] -= a[i][b] a[b][j]               (i, j != b; new row)
+//   column block    a[i][b] = -a[i][b] D^-1                 (i != b)
+//   diagonal        a[b][b] = D^-1.
+// No pivoting: the pivots are diagonal blocks of Schur complements of the
+// symmetric I + A_t, whose eigenvalues stay >= 1.
+__device__ __forceinline__ void tile_product(float (&a)[kD][kPad], int mr, int mk, int nk, int nc,
+                                             const float (*x)[33], bool x_is_dinv, f32x16& acc,
+                                             int lane) {
+  // acc += X Y, X = 32 x 32 (rows mr.., cols mk.. of a, or dinv), Y = a[nk..][nc..]
+  const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int s2 = 0; s2 < 32; s2 += 2) {
+    const float av = x_is_dinv ? x[l32][s2 + half] : a[mr + l32][mk + s2 + half];
+    acc = mfma(av, a[nk + s2 + half][nc + l32], acc);
+  }
+}
+
 __global__ __launch_bounds__(256) void vda_inverse_kernel(const float* __restrict__ A,
                                                           const float* __restrict__ alpha,
                                                           float* __restrict__ M,
                                                           float* __restrict__ P) {
-  __shared__ float colk[2][2][kD / 2];   // [buffer][row parity][row / 2]: a[row][k] before step k
-  __shared__ float rowk[2][kD];          // [buffer][column]: a[k][column] before step k
+  __shared__ float a[kD][kPad];
+  __shared__ float dinv[32][33];
   const size_t m = (size_t)blockIdx.y * gridDim.x + blockIdx.x;   // h * frames + t
-  const int tid = threadIdx.x, j = tid & (kD - 1), p = tid >> 7;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31;
   const float* src = A + m * kMat;
-  float r[kD / 2];
+  for (int x = tid; x < kMat; x += 256) {
+    const int i = x >> 7, j = x & (kD - 1);
+    a[i][j] = src[x] + (i == j ? 1.f : 0.f);
+  }
+  __syncthreads();
+  for (int b = 0; b < 4; ++b) {
+    const int b0 = 32 * b;
+    // D^-1 by wave 0: unblocked in-place elimination of the 32 x 32 block
+    if (w == 0) {
+      for (int x = lane; x < 32 * 32; x += 64) dinv[x >> 5][x & 31] = a[b0 + (x >> 5)][b0 + (x & 31)];
+      for (int k = 0; k < 32; ++k) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the block is in LDS for every lane
+        const float piv_inv = 1.f / dinv[k][k];
+        const float ck = dinv[l32][k];        // column k, read before it changes
+        const int c0 = (lane >> 5) * 16;      // this lane updates row l32, columns c0..c0+15
+        float rowk[16];
 #pragma unroll
-  for (int i = 0; i < kD / 2; ++i) r[i] = src[(2 * i + p) * kD + j] + (2 * i + p == j ? 1.f : 0.f);
-  for (int k = 0; k < kD; ++k) {
-    const int buf = k & 1;
-    if (j == k) {
+        for (int c = 0; c < 16; ++c) rowk[c] = (c0 + c == k ? 1.f : dinv[k][c0 + c]) * piv_inv;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int i = 0; i < kD / 2; ++i) colk[buf][p][i] = r[i];
-    }
-    if (p == (k & 1)) {
-      // this thread holds a[k][j] in r[k / 2]; select it without dynamic indexing
-      float x = 0.f;
-#pragma unroll
-      for (int i = 0; i < kD / 2; ++i) x = (i == (k >> 1)) ? r[i] : x;
-      rowk[buf][j] = x;
+        for (int c = 0; c < 16; ++c) {
+          const int col = c0 + c;
+          dinv[l32][col] = l32 == k ? rowk[c] : (col == k ? 0.f : dinv[l32][col]) - ck * rowk[c];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     __syncthreads();
-    const float piv_inv = 1.f / colk[buf][k & 1][k >> 1];
-    const float rk = (j == k ? 1.f : rowk[buf][j]) * piv_inv;     // scaled row k, a[k][k] = 1 / pivot
+    // row block: a[b][j] = D^-1 a[b][j], one tile per wave (j != b)
+    {
+      const int jb = w < b ? w : w + 1;
+      f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < kD / 2; ++i) {
-      const int row = 2 * i + p;
-      r[i] = row == k ? rk : (j == k ? 0.f : r[i]) - colk[buf][p][i] * rk;
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      if (w < 3) tile_product(a, 0, 0, b0, 32 * jb, dinv, true, acc, lane);
+      __syncthreads();   // every wave has read the old row block
+      if (w < 3)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[b0 + acc_row(r, lane)][32 * jb + l32] = acc[r];
+      __syncthreads();
+    }
+    // trailing blocks: a[i][j] -= a[i][b] a[b][j], nine tiles over the four waves
+    for (int t = w; t < 9; t += 4) {
+      const int ib0 = t / 3, jb0 = t % 3;
+      const int ib = ib0 < b ? ib0 : ib0 + 1, jb = jb0 < b ? jb0 : jb0 + 1;
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = -a[32 * ib + acc_row(r, lane)][32 * jb + l32];
+      tile_product(a, 32 * ib, b0, b0, 32 * jb, dinv, false, acc, lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[32 * ib + acc_row(r, lane)][32 * jb + l32] = -acc[r];
+    }
+    __syncthreads();
+    // column block: a[i][b] = -a[i][b] D^-1 (i != b); diagonal a[b][b] = D^-1
+    {
+      const int ib = w < b ? w : w + 1;
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      if (w < 3) {
+        // acc = a[i][b] D^-1: X = a[ib][b] (A operand), Y = dinv (B operand)
+#pragma unroll
+        for (int s2 = 0; s2 < 32; s2 += 2) {
+          const int half = lane >> 5;
+          acc = mfma(a[32 * ib + l32][b0 + s2 + half], dinv[s2 + half][l32], acc);
+        }
+      }
+      __syncthreads();   // the old column block has been read
+      if (w < 3) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[32 * ib + acc_row(r, lane)][b0 + l32] = -acc[r];
+      } else {
+        for (int x = lane; x < 32 * 32; x += 64) a[b0 + (x >> 5)][b0 + (x & 31)] = dinv[x >> 5][x & 31];
+      }
+      __syncthreads();
     }
   }
   const float* al = alpha + m * kD;
   float* mo = M + m * kMat;
   float* po = P + m * kMat;
-#pragma unroll
-  for (int i = 0; i < kD / 2; ++i) {
-    const int row = 2 * i + p;
-    mo[row * kD + j] = r[i];
-    po[row * kD + j] = al[row] * r[i];
+  for (int x = tid; x < kMat; x += 256) {
+    const int i = x >> 7, j = x & (kD - 1);
+    mo[x] = a[i][j];
+    po[x] = al[i] * a[i][j];
   }
 }
 
@@ -214,20 +284,27 @@ __global__ __launch_bounds__(1024) void vda_scan_kernel(const float* __restrict_
   }
 }
 
-// out rows of frame f: o = (fwd[lo] + rev[hi]) q.  One workgroup per (frame,
-// head): W = fwd[lo] + rev[hi] is staged once in LDS, then 128 query rows at a
-// time pass through LDS (wave w owns 32 of them).
-constexpr int kQPitch = kD + 2;   // bf16 row pitch of staged queries: 65 words, 32 rows -> 32 banks
+// out rows of frame f: o = (fwd[lo] + rev[hi]) q on the bf16 matrix cores.  q is
+// bf16 already; W = fwd[lo] + rev[hi] is split into W_hi = bf16(W) and W_lo =
+// bf16(W - W_hi), |W - W_hi - W_lo| <= 2^-18 |W|, and o = W_hi q + W_lo q with
+// fp32 accumulation.  In the transposed product O^T = W Q^T both operands are
+// row-contiguous: lane l of v_mfma_f32_32x32x16_bf16 takes 8 consecutive head
+// dims of row l % 32 of W (from LDS) and of query l % 32 (from global).  One
+// workgroup per (frame, head); wave w covers query tiles w, w + 4, ...
+constexpr int kWPitch = kD + 8;   // bf16 row pitch of the staged W halves: 16-byte chunks rotate per row
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __restrict__ Q,
                                                           const float* __restrict__ fwd,
                                                           const float* __restrict__ rev, int ft,
                                                           int frames, int chunk, int nb,
                                                           float* __restrict__ out) {
-  __shared__ float W[kD][kPad];
-  __shared__ __attribute__((aligned(16))) uint16_t qs[kD][kQPitch];
+  __shared__ __attribute__((aligned(16))) __bf16 w_hi[kD][kWPitch];
+  __shared__ __attribute__((aligned(16))) __bf16 w_lo[kD][kWPitch];
   const int f = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, g = lane >> 5;
   int lo = 0, hi = frames;
   if (f != 0 && f != frames - 1) {
     const int c = f / chunk;
@@ -238,42 +315,49 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __rest
   }
   const float* wf = fwd + ((size_t)h * (frames + 1) + lo) * kMat;
   const float* wr = rev + ((size_t)h * (frames + 1) + hi) * kMat;
-  for (int i = tid >> 7; i < kD; i += 2) {
-    const int j = tid & (kD - 1);
-    W[i][j] = wf[i * kD + j] + wr[i * kD + j];
+  for (int x = tid; x < kMat; x += 256) {
+    const int i = x >> 7, j = x & (kD - 1);
+    const float wv = wf[x] + wr[x];
+    const __bf16 h16 = (__bf16)wv;
+    w_hi[i][j] = h16;
+    w_lo[i][j] = (__bf16)(wv - (float)h16);
   }
+  __syncthreads();
   const size_t N = (size_t)frames * ft;
   const uint16_t* qf = Q + ((size_t)h * N + (size_t)f * ft) * kD;
   float* of = out + ((size_t)h * N + (size_t)f * ft) * kD;
-  for (int r0 = 0; r0 < ft; r0 += kD) {
-    __syncthreads();   // W staged / previous rows consumed
-    // 128 rows x 128 bf16: thread tid copies 4 B at (row, pair) for 16 passes
-    for (int x = tid; x < kD * kD / 2; x += 256) {
-      const int row = x >> 6, pr = x & 63;
-      const uint32_t v =
-          r0 + row < ft ? *(const uint32_t*)(qf + (size_t)(r0 + row) * kD + 2 * pr) : 0u;
-      *(uint32_t*)&qs[row][2 * pr] = v;
-    }
-    __syncthreads();
-    f32x16 acc[4];
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qf), (short)0, ft * kD * 2, 0x00020000);
+  const int ntiles = (ft + 31) / 32;
+  for (int nt = w; nt < ntiles; nt += 4) {
+    const int qrow = 32 * nt + l32;
+    // B operand: query qrow, dims 16 kt + 8 g + 0..7 (rows past ft read zeros)
+    bf16x8 qb[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int kt = 0; kt < 8; ++kt)
+      qb[kt] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, qrow * kD * 2 + 32 * kt + 16 * g, 0, 0));
+#pragma unroll 1
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-#pragma unroll 4
-    for (int s2 = 0; s2 < kD; s2 += 2) {
-      const int d = s2 + half;
-      const float av = bf16f(qs[32 * w + l32][d]);
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma(av, W[32 * j + l32][d], acc[j]);   // W^T[d][dv] = W[dv][d]
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = r0 + 32 * w + acc_row(r, lane);
-        if (rr < ft) of[(size_t)rr * kD + 32 * j + l32] = acc[j][r];
+      for (int kt = 0; kt < 8; ++kt) {
+        const bf16x8 ah = *(const bf16x8*)&w_hi[32 * mt + l32][16 * kt + 8 * g];
+        const bf16x8 al = *(const bf16x8*)&w_lo[32 * mt + l32][16 * kt + 8 * g];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qb[kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qb[kt], acc, 0, 0, 0);
       }
+      // acc[4 j + i]: head dim 32 mt + 8 j + 4 g + i of query qrow
+      if (qrow < ft) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v4 = {acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+          *(f32x4*)(of + (size_t)qrow * kD + 32 * mt + 8 * j + 4 * g) = v4;
+        }
+      }
+    }
   }
 }
 
