@@ -54,39 +54,108 @@ __device__ __forceinline__ void store_row_tile(float* __restrict__ m, int rt, co
     for (int r = 0; r < 16; ++r) m[(32 * rt + acc_row(r, lane)) * kD + 32 * j + (lane & 31)] = acc[j][r];
 }
 
-// A_t and B_t of frame t of head h.  Wave w owns row tile w of both.
+// A_t and B_t of frame t of head h on the bf16 matrix cores: with X = beta K
+// and Y = beta V split into bf16 hi + lo parts (residual <= 2^-18 of each
+// value), A_t = X_hi^T K + X_lo^T K and B_t = Y_hi^T K + Y_lo^T K, fp32
+// accumulation (K is bf16 already).  The frame streams through LDS in 64-token
+// chunks of five tiles (K, X_hi, X_lo, Y_hi, Y_lo), rows of 256 B with 16-byte
+// chunks XOR-swizzled by v_swz.  Every MFMA operand is 8 tokens of one head
+// dim, read with ds_read_b64_tr_b16; both operands use the same addressing,
+// so they agree on which token each reduction index holds.  Wave w owns row
+// tile w of A_t and of B_t (8 accumulator tiles).
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2s __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kChunk = 64;               // tokens per LDS chunk
+constexpr int kTileB = kChunk * kD * 2;  // bytes of one chunk tile
+
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
 __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
                                                         const float* __restrict__ beta, int ft,
                                                         int frames, float* __restrict__ A,
                                                         float* __restrict__ B) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[5][kTileB];   // K, X_hi, X_lo, Y_hi, Y_lo
   const int t = blockIdx.x, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t N = (size_t)frames * ft;
   const size_t tok0 = (size_t)h * N + (size_t)t * ft;
+  // transpose-read offset of head-dim block db: lane group G = lane >> 4 covers
+  // dims 32 db + 16 (G & 1) + 0..15 and tokens 16 (G >> 1) + 8 s + 0..7 of a
+  // 32-token half; source lane s16 reads 4 dims of token (s16 >> 2) (then + 4)
+  int voff[4];
+  {
+    const int s16 = lane & 15, G = lane >> 4;
+    const int vkey = 16 * (G >> 1) + (s16 >> 2);
+    const int vdim = 16 * (G & 1) + 4 * (s16 & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int dim = vdim + 32 * db;
+      voff[db] = vkey * kD * 2 + (((dim >> 3) ^ v_swz(vkey)) << 4) + 8 * ((dim >> 2) & 1);
+    }
+  }
+  auto frag = [&](int tile, int db, int st) -> bf16x8s {
+    const unsigned char* r0 = lds[tile] + voff[db] + (32 * (st >> 1) + 8 * (st & 1)) * kD * 2;
+    const u32x2s lo = __builtin_bit_cast(u32x2s, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)r0));
+    const u32x2s hi = __builtin_bit_cast(
+        u32x2s, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(r0 + 4 * kD * 2)));
+    const u32x4s x = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8s, x);
+  };
   f32x16 acc_a[4], acc_b[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc_a[j][r] = 0.f; acc_b[j][r] = 0.f; }
-  for (int u0 = 0; u0 < ft; u0 += 2) {
-    const int u = u0 + half;
-    float kv[4], vw = 0.f, b = 0.f;
-    if (u < ft) {
-      const uint16_t* kr = K + (tok0 + u) * kD;
+  for (int u0 = 0; u0 < ft; u0 += kChunk) {
+    __syncthreads();   // the previous chunk has been consumed
+    // stage: 64 tokens x 16 chunks of 8 dims, 4 per thread
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kv[j] = bf16f(kr[32 * j + l32]);
-      vw = bf16f(V[(tok0 + u) * kD + 32 * w + l32]);
-      b = beta[tok0 + u];
-    } else {
+    for (int x = 0; x < 4; ++x) {
+      const int pos = tid + 256 * x, row = pos >> 4, c = pos & 15;
+      const int u = u0 + row;
+      u32x4s kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+      float b = 0.f;
+      if (u < ft) {
+        kw = *(const u32x4s*)(K + (tok0 + u) * kD + 8 * c);
+        vw = *(const u32x4s*)(V + (tok0 + u) * kD + 8 * c);
+        b = beta[tok0 + u];
+      }
+      bf16x8s xh, xl, yh, yl;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kv[j] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t kk = kw[e >> 1], vv = vw[e >> 1];
+        const float kf = __uint_as_float((e & 1) ? (kk & 0xffff0000u) : (kk << 16));
+        const float vf = __uint_as_float((e & 1) ? (vv & 0xffff0000u) : (vv << 16));
+        const float xk = b * kf, yv = b * vf;
+        xh[e] = (__bf16)xk;
+        xl[e] = (__bf16)(xk - (float)xh[e]);
+        yh[e] = (__bf16)yv;
+        yl[e] = (__bf16)(yv - (float)yh[e]);
+      }
+      const int off = row * kD * 2 + ((c ^ v_swz(row)) << 4);
+      *(u32x4s*)(lds[0] + off) = kw;
+      *(bf16x8s*)(lds[1] + off) = xh;
+      *(bf16x8s*)(lds[2] + off) = xl;
+      *(bf16x8s*)(lds[3] + off) = yh;
+      *(bf16x8s*)(lds[4] + off) = yl;
     }
-    const float ka = b * kv[w], va = b * vw;    // beta_u k_u[32 w + i], beta_u v_u[32 w + i]
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc_a[j] = mfma(ka, kv[j], acc_a[j]);
-      acc_b[j] = mfma(va, kv[j], acc_b[j]);
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8s xh = frag(1, w, st), xl = frag(2, w, st), yh = frag(3, w, st), yl = frag(4, w, st);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8s kf = frag(0, j, st);
+        acc_a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, kf, acc_a[j], 0, 0, 0);
+        acc_a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, kf, acc_a[j], 0, 0, 0);
+        acc_b[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yh, kf, acc_b[j], 0, 0, 0);
+        acc_b[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(yl, kf, acc_b[j], 0, 0, 0);
+      }
     }
   }
   const size_t off = ((size_t)h * frames + t) * kMat;
