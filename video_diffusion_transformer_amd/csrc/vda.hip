@@ -6,8 +6,8 @@
 //   A_t = sum_u beta_u k_u k_u^T,  B_t = sum_u beta_u v_u k_u^T,
 //   S_t = (S_prev Diag(alpha_t) + B_t)(I + A_t)^-1 = S_prev P_t + C_t
 // with M_t = (I + A_t)^-1, P_t = Diag(alpha_t) M_t and C_t = B_t M_t.  Everything
-// but the last line is independent per frame, so it runs for all frames at
-// once; only S_t = S_prev P_t + C_t is sequential.  The forward scan writes
+// but the last line is independent per frame, so it runs for all interior
+// frames at once; only S_t = S_prev P_t + C_t is sequential.  The forward scan writes
 // frames 1..F-2 in order, the reverse scan F-2..1, both from S_text / 2 (the
 // first and last frames are softmax anchors and are not written).  A query of
 // frame f reads o = fwd[lo(f)] q + rev[hi(f)] q, lo / hi the frames just
@@ -15,8 +15,8 @@
 //
 // Every product is fp32 on the matrix cores (v_mfma_f32_32x32x2_f32: lane l
 // holds A[l % 32][l / 32] and B[l / 32][l % 32]); the inverse is an in-place
-// Gauss-Jordan elimination in LDS, which needs no pivoting because I + A_t is
-// symmetric with eigenvalues >= 1.
+// Gauss-Jordan elimination held in the matrix-core accumulators, which needs
+// no pivoting because I + A_t is symmetric with eigenvalues >= 1.
 //
 // Kernels: vda_stats_kernel (A_t, B_t per frame), vda_inverse_kernel (M_t and
 // P_t), vda_matmul_kernel (C_t = B_t M_t), vda_scan_kernel (one workgroup per
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
                                                         int frames, float* __restrict__ A,
                                                         float* __restrict__ B) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[5][kTileB];   // K, X_hi, X_lo, Y_hi, Y_lo
-  const int t = blockIdx.x, h = blockIdx.y;
+  const int t = blockIdx.x + 1, h = blockIdx.y;   // interior frames only
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t N = (size_t)frames * ft;
   const size_t tok0 = (size_t)h * N + (size_t)t * ft;
@@ -163,132 +163,140 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
   store_row_tile(B + off, w, acc_b, lane);
 }
 
-// M_t = (I + A_t)^-1 by blocked Gauss-Jordan in place, and P_t = Diag(alpha_t)
-// M_t.  Four steps over 32-column blocks b: D = a[b][b] is inverted by one wave
-// (unblocked elimination of the 32 x 32 block), then, as 32 x 32 tile products
-// on the matrix cores (k = 32):
-//   row block       a[b][j] = D^-1 a[b][j]                  (j != b)
-//   trailing blocks a[i][j] -= a[i][b] a[b][j]               (i, j != b; new row)
-//   column block    a[i][b] = -a[i][b] D^-1                 (i != b)
-//   diagonal        a[b][b] = D^-1.
-// No pivoting: the pivots are diagonal blocks of Schur complements of the
-// symmetric I + A_t, whose eigenvalues stay >= 1.
-__device__ __forceinline__ void tile_product(float (&a)[kD][kPad], int mr, int mk, int nk, int nc,
-                                             const float (*x)[33], bool x_is_dinv, f32x16& acc,
-                                             int lane) {
-  // acc += X Y, X = 32 x 32 (rows mr.., cols mk.. of a, or dinv), Y = a[nk..][nc..]
-  const int l32 = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int s2 = 0; s2 < 32; s2 += 2) {
-    const float av = x_is_dinv ? x[l32][s2 + half] : a[mr + l32][mk + s2 + half];
-    acc = mfma(av, a[nk + s2 + half][nc + l32], acc);
-  }
-}
-
-__global__ __launch_bounds__(256) void vda_inverse_kernel(const float* __restrict__ A,
-                                                          const float* __restrict__ alpha,
-                                                          float* __restrict__ M,
-                                                          float* __restrict__ P) {
-  __shared__ float a[kD][kPad];
-  __shared__ float dinv[32][33];
-  const size_t m = (size_t)blockIdx.y * gridDim.x + blockIdx.x;   // h * frames + t
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31;
+// M_t = (I + A_t)^-1 by Gauss-Jordan elimination in place, four pivots per
+// step, and P_t = Diag(alpha_t) M_t.  The matrix never leaves the fp32
+// matrix-core accumulators: wave w holds tiles (w, 0..3).  Step q pivots on
+// K = {4q..4q+3} with the 4 x 4 block P = a[K][K] and Pinv = P^-1:
+//   a[K][j] <- Pinv a[K][j] (j not in K),   a[K][K] <- Pinv,
+//   a[i][j] <- a[i][j] - a[i][K] Pinv a[K][j],   a[i][K] <- -a[i][K] Pinv   (i not in K),
+// which is a single rank-4 update a <- a0 - C R, where a0 is a with row K and
+// column K zeroed, C = a[:][K] except C[K][K] = -I, and R = Pinv a[K][:] except
+// R[K][K] = Pinv (two v_mfma_f32_32x32x2_f32 per tile).  No pivoting: every P
+// is a Schur complement of the symmetric I + A_t, so its eigenvalues stay >= 1.
+// Row K reaches every wave through LDS (double buffered: one barrier per
+// step); column K stays within each wave; every lane inverts P itself.
+// Interior frames only (blockIdx.x + 1): the scans never read the anchors.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void vda_inverse_kernel(const float* __restrict__ A, const float* __restrict__ alpha, int frames,
+                        float* __restrict__ M, float* __restrict__ P) {
+  __shared__ f32x4 rows[2][kD];       // rows[buf][col] = a[4q + 0..3][col]
+  __shared__ float cols[4][32][5];    // wave w: a[32 w + row][4q + 0..3], pitch 5
+  const size_t m = (size_t)blockIdx.y * frames + blockIdx.x + 1;   // h * frames + t
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const float* src = A + m * kMat;
-  for (int x = tid; x < kMat; x += 256) {
-    const int i = x >> 7, j = x & (kD - 1);
-    a[i][j] = src[x] + (i == j ? 1.f : 0.f);
-  }
-  __syncthreads();
-  for (int b = 0; b < 4; ++b) {
-    const int b0 = 32 * b;
-    // D^-1 by wave 0: unblocked in-place elimination of the 32 x 32 block
-    if (w == 0) {
-      for (int x = lane; x < 32 * 32; x += 64) dinv[x >> 5][x & 31] = a[b0 + (x >> 5)][b0 + (x & 31)];
-      for (int k = 0; k < 32; ++k) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the block is in LDS for every lane
-        const float piv_inv = 1.f / dinv[k][k];
-        const float ck = dinv[l32][k];        // column k, read before it changes
-        const int c0 = (lane >> 5) * 16;      // this lane updates row l32, columns c0..c0+15
-        float rowk[16];
+  f32x16 acc[4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) rowk[c] = (c0 + c == k ? 1.f : dinv[k][c0 + c]) * piv_inv;
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+  for (int T = 0; T < 4; ++T)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const int col = c0 + c;
-          dinv[l32][col] = l32 == k ? rowk[c] : (col == k ? 0.f : dinv[l32][col]) - ck * rowk[c];
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * w + acc_row(r, lane), col = 32 * T + l32;
+      acc[T][r] = src[row * kD + col] + (row == col ? 1.f : 0.f);
+    }
+#pragma unroll
+  for (int q = 0; q < 32; ++q) {
+    const int J = q >> 3, s = q & 7;            // tile / band holding K; 4-row group in it
+    const int rr = 4 * (s >> 1), hs = s & 1;    // rows 4s..4s+3: registers rr.., half hs
+    f32x4* rb = rows[q & 1];
+    const int cm = l32 - 4 * s;                 // offset of this lane's column (row) in K
+    const bool in_k = cm >= 0 && cm < 4;
+    if (w == J && half == hs) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const f32x4 v = {acc[T][rr], acc[T][rr + 1], acc[T][rr + 2], acc[T][rr + 3]};
+        rb[32 * T + l32] = v;
       }
+    }
+    if (in_k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cols[w][acc_row(r, lane)][cm] = acc[J][r];
     }
     __syncthreads();
-    // row block: a[b][j] = D^-1 a[b][j], one tile per wave (j != b)
-    {
-      const int jb = w < b ? w : w + 1;
-      f32x16 acc;
+    // Pinv, in place: pv[i][j] = a[4q + i][4q + j] = rb[4q + j][i]
+    float pv[4][4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      if (w < 3) tile_product(a, 0, 0, b0, 32 * jb, dinv, true, acc, lane);
-      __syncthreads();   // every wave has read the old row block
-      if (w < 3)
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const f32x4 c = rb[4 * q + j2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a[b0 + acc_row(r, lane)][32 * jb + l32] = acc[r];
-      __syncthreads();
+      for (int i2 = 0; i2 < 4; ++i2) pv[i2][j2] = c[i2];
     }
-    // trailing blocks: a[i][j] -= a[i][b] a[b][j], nine tiles over the four waves
-    for (int t = w; t < 9; t += 4) {
-      const int ib0 = t / 3, jb0 = t % 3;
-      const int ib = ib0 < b ? ib0 : ib0 + 1, jb = jb0 < b ? jb0 : jb0 + 1;
-      f32x16 acc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = -a[32 * ib + acc_row(r, lane)][32 * jb + l32];
-      tile_product(a, 32 * ib, b0, b0, 32 * jb, dinv, false, acc, lane);
+    for (int p2 = 0; p2 < 4; ++p2) {
+      const float d = 1.f / pv[p2][p2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) a[32 * ib + acc_row(r, lane)][32 * jb + l32] = -acc[r];
+      for (int j2 = 0; j2 < 4; ++j2)
+        if (j2 != p2) pv[p2][j2] *= d;
+      pv[p2][p2] = d;
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        if (i2 == p2) continue;
+        const float f = pv[i2][p2];
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2)
+          if (j2 != p2) pv[i2][j2] = fmaf(-f, pv[p2][j2], pv[i2][j2]);
+        pv[i2][p2] = -f * d;
+      }
     }
-    __syncthreads();
-    // column block: a[i][b] = -a[i][b] D^-1 (i != b); diagonal a[b][b] = D^-1
-    {
-      const int ib = w < b ? w : w + 1;
-      f32x16 acc;
+    // B operands R[2 h + half][32 T + l32]; the columns of K read as the identity
+    float pr[2][4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      if (w < 3) {
-        // acc = a[i][b] D^-1: X = a[ib][b] (A operand), Y = dinv (B operand)
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int s2 = 0; s2 < 32; s2 += 2) {
-          const int half = lane >> 5;
-          acc = mfma(a[32 * ib + l32][b0 + s2 + half], dinv[s2 + half][l32], acc);
-        }
+      for (int i2 = 0; i2 < 4; ++i2) pr[h2][i2] = half ? pv[2 * h2 + 1][i2] : pv[2 * h2][i2];
+    float rv[4][2];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      f32x4 raw = rb[32 * T + l32];
+      if (T == J && in_k) {
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) raw[i2] = cm == i2 ? 1.f : 0.f;
       }
-      __syncthreads();   // the old column block has been read
-      if (w < 3) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a[32 * ib + acc_row(r, lane)][b0 + l32] = -acc[r];
-      } else {
-        for (int x = lane; x < 32 * 32; x += 64) a[b0 + (x >> 5)][b0 + (x & 31)] = dinv[x >> 5][x & 31];
-      }
-      __syncthreads();
+      for (int h2 = 0; h2 < 2; ++h2)
+        rv[T][h2] = pr[h2][0] * raw[0] + pr[h2][1] * raw[1] + pr[h2][2] * raw[2] + pr[h2][3] * raw[3];
+    }
+    // A operands -C[l32][2 h + half]; the rows of K read as +I
+    float cv[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float c = cols[w][l32][2 * h2 + half];
+      cv[h2] = (w == J && in_k) ? (cm == 2 * h2 + half ? 1.f : 0.f) : -c;
+    }
+    if (in_k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[J][r] = 0.f;
+    }
+    if (w == J && half == hs) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) acc[T][rr + i2] = 0.f;
+    }
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      acc[T] = mfma(cv[0], rv[T][0], acc[T]);
+      acc[T] = mfma(cv[1], rv[T][1], acc[T]);
     }
   }
   const float* al = alpha + m * kD;
   float* mo = M + m * kMat;
   float* po = P + m * kMat;
-  for (int x = tid; x < kMat; x += 256) {
-    const int i = x >> 7, j = x & (kD - 1);
-    mo[x] = a[i][j];
-    po[x] = al[i] * a[i][j];
-  }
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * w + acc_row(r, lane), col = 32 * T + l32;
+      mo[row * kD + col] = acc[T][r];
+      po[row * kD + col] = al[row] * acc[T][r];
+    }
 }
 
-// out[b] = X[b] Y[b] for batches of 128 x 128 matrices.  Wave w owns row tile w.
+// out[b] = X[b] Y[b] for the interior frames' 128 x 128 matrices, b = h * frames
+// + t.  Wave w owns row tile w.
 __global__ __launch_bounds__(256) void vda_matmul_kernel(const float* __restrict__ X,
-                                                         const float* __restrict__ Y,
+                                                         const float* __restrict__ Y, int frames,
                                                          float* __restrict__ out) {
   __shared__ float xs[kD][kPad];
-  const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const size_t b = (size_t)blockIdx.y * frames + blockIdx.x + 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const float* x = X + b * kMat;
   const float* y = Y + b * kMat;
@@ -442,10 +450,14 @@ hipError_t launch_vda_states(const uint16_t* k, const uint16_t* v, const float* 
   float* M = B + per;
   float* P = M + per;
   float* C = P + per;
-  const dim3 grid(frames, heads);
-  hipLaunchKernelGGL(vda_stats_kernel, grid, dim3(256), 0, stream, k, v, beta, ft, frames, A, B);
-  hipLaunchKernelGGL(vda_inverse_kernel, grid, dim3(256), 0, stream, A, alpha, M, P);
-  hipLaunchKernelGGL(vda_matmul_kernel, grid, dim3(256), 0, stream, B, M, C);
+  // frame statistics, inverses and C_t for the interior frames 1..frames-2
+  // (the first and last frames are never written into a state)
+  if (frames > 2) {
+    const dim3 grid(frames - 2, heads);
+    hipLaunchKernelGGL(vda_stats_kernel, grid, dim3(256), 0, stream, k, v, beta, ft, frames, A, B);
+    hipLaunchKernelGGL(vda_inverse_kernel, grid, dim3(256), 0, stream, A, alpha, frames, M, P);
+    hipLaunchKernelGGL(vda_matmul_kernel, grid, dim3(256), 0, stream, B, M, frames, C);
+  }
   hipLaunchKernelGGL(vda_scan_kernel, dim3(heads, 2), dim3(1024), 0, stream, P, C, s_text, frames, fwd,
                      rev);
   return hipGetLastError();
