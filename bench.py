@@ -336,9 +336,14 @@ def main():
                 a_ms.append(a_ev[0].elapsed_time(a_ev[1]))
         del vin, vout
         am = float(np.median(a_ms))
+        # algorithmic FLOP: A_t and B_t over the interior frames' tokens (the
+        # anchors are never written), the readout (one product with the summed
+        # states per token), and per interior frame the inverse (2 d^3), C_t =
+        # B_t M_t (2 d^3) and one state product in each scan (2 x 2 d^3)
         d2 = 128.0 * 128.0
-        flop_a = (4.0 * TOKENS * d2 + 2.0 * TOKENS * d2) * HEADS \
-            + (2.0 + 2.0) * 128.0 * d2 * frames * HEADS + 2 * 2.0 * 128.0 * d2 * (frames - 2) * HEADS
+        inner = frames - 2
+        flop_a = (4.0 * inner * FRAME_TOKENS * d2 + 2.0 * TOKENS * d2) * HEADS \
+            + (2.0 + 2.0) * 128.0 * d2 * inner * HEADS + 2 * 2.0 * 128.0 * d2 * inner * HEADS
         vda = {"ms": round(am, 3), "flop": flop_a, "tflops": round(flop_a / (am * 1e-3) / 1e12, 2),
                "frac_peak_fp32_mfma": round(flop_a / (am * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
                "frames": frames, "frame_tokens": FRAME_TOKENS}

@@ -19,8 +19,8 @@
 // no pivoting because I + A_t is symmetric with eigenvalues >= 1.
 //
 // Kernels: vda_stats_kernel (A_t, B_t per frame), vda_inverse_kernel (M_t and
-// P_t), vda_matmul_kernel (C_t = B_t M_t), vda_scan_kernel (one workgroup per
-// head and direction, the state in LDS), vda_readout_kernel.
+// P_t^T), vda_matmul_kernel (C_t = B_t M_t), vda_scan_kernel (one workgroup per
+// head, direction and 32-row band of the state), vda_readout_kernel.
 
 #include "fvattn_internal.h"
 
@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
 }
 
 // M_t = (I + A_t)^-1 by Gauss-Jordan elimination in place, four pivots per
-// step, and P_t = Diag(alpha_t) M_t.  The matrix never leaves the fp32
+// step, and P_t^T for P_t = Diag(alpha_t) M_t (M_t is symmetric, so P_t^T[i][j]
+// = alpha_t[j] M_t[i][j]).  The matrix never leaves the fp32
 // matrix-core accumulators: wave w holds tiles (w, 0..3).  Step q pivots on
 // K = {4q..4q+3} with the 4 x 4 block P = a[K][K] and Pinv = P^-1:
 //   a[K][j] <- Pinv a[K][j] (j not in K),   a[K][K] <- Pinv,
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
 // Interior frames only (blockIdx.x + 1): the scans never read the anchors.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void vda_inverse_kernel(const float* __restrict__ A, const float* __restrict__ alpha, int frames,
-                        float* __restrict__ M, float* __restrict__ P) {
+                        float* __restrict__ M, float* __restrict__ PT) {
   __shared__ f32x4 rows[2][kD];       // rows[buf][col] = a[4q + 0..3][col]
   __shared__ float cols[4][32][5];    // wave w: a[32 w + row][4q + 0..3], pitch 5
   const size_t m = (size_t)blockIdx.y * frames + blockIdx.x + 1;   // h * frames + t
@@ -279,15 +280,17 @@ void vda_inverse_kernel(const float* __restrict__ A, const float* __restrict__ a
   }
   const float* al = alpha + m * kD;
   float* mo = M + m * kMat;
-  float* po = P + m * kMat;
+  float* po = PT + m * kMat;
 #pragma unroll
-  for (int T = 0; T < 4; ++T)
+  for (int T = 0; T < 4; ++T) {
+    const float ac = al[32 * T + l32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * w + acc_row(r, lane), col = 32 * T + l32;
       mo[row * kD + col] = acc[T][r];
-      po[row * kD + col] = al[row] * acc[T][r];
+      po[row * kD + col] = ac * acc[T][r];
     }
+  }
 }
 
 // out[b] = X[b] Y[b] for the interior frames' 128 x 128 matrices, b = h * frames
@@ -316,49 +319,70 @@ __global__ __launch_bounds__(256) void vda_matmul_kernel(const float* __restrict
   store_row_tile(out + b * kMat, w, acc, lane);
 }
 
-// One workgroup per (head, direction): S = S_text / 2, then S = S P_t + C_t over
-// the written frames; states [head][frames + 1] of each direction.  Sixteen
-// waves, one 32 x 32 output tile each (row tile w % 4, column tile w / 4): the
-// chains are sequential, so each step is spread as wide as it goes.
-__global__ __launch_bounds__(1024) void vda_scan_kernel(const float* __restrict__ P,
-                                                        const float* __restrict__ C,
-                                                        const float* __restrict__ s_text,
-                                                        int frames, float* __restrict__ fwd,
-                                                        float* __restrict__ rev) {
-  __shared__ float S[kD][kPad];
-  const int h = blockIdx.x, dir = blockIdx.y;   // 0 forward, 1 reverse
+// The scans: S_t = S_prev P_t + C_t over the interior frames, forward from
+// fwd[0] = S_text / 2 and reverse from rev[F] = S_text / 2; every state is
+// stored (anchor frames pass the state on unchanged).  Rows of S never mix, so
+// a workgroup runs one head, one direction and one 32-row band of the state.
+// Wave w owns column tile w: its B operands are rows 32 w.. of P_t^T (64
+// consecutive k per lane) and its accumulator starts from C_t's tile, both
+// loaded into registers one frame ahead; the band (the A operand) is in LDS.
+// Lane half g takes k = 64 g + i in product i.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void vda_scan_kernel(const float* __restrict__ PT, const float* __restrict__ C,
+                     const float* __restrict__ s_text, int frames, float* __restrict__ fwd,
+                     float* __restrict__ rev) {
+  __shared__ float S[32][kPad];
+  const int rb = blockIdx.x, h = blockIdx.y, dir = blockIdx.z;   // dir 0 forward, 1 reverse
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
-  const int rt = w & 3, ct = w >> 2;
-  const int j0 = tid & (kD - 1), i0 = tid >> 7;   // copy pattern: 8 rows per pass
   float* states = (dir == 0 ? fwd : rev) + (size_t)h * (frames + 1) * kMat;
   const float* st = s_text + (size_t)h * kMat;
-  const int first = dir == 0 ? 0 : frames;      // index of the seed state
-  for (int i = i0; i < kD; i += 8) {
-    const float x = 0.5f * st[i * kD + j0];
-    S[i][j0] = x;
-    states[(size_t)first * kMat + i * kD + j0] = x;
+  auto frame_of = [&](int step) { return dir == 0 ? step : frames - 1 - step; };
+  auto dst_of = [&](int step) { return dir == 0 ? step + 1 : frames - 1 - step; };
+  // this lane's elements of its tile: rows 32 rb + acc_row(r), column 32 w + l32
+  auto store = [&](int idx, const f32x16& x) {
+    float* so = states + (size_t)idx * kMat + 32 * w + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) so[(32 * rb + acc_row(r, lane)) * kD] = x[r];
+  };
+  f32x16 cur;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * rb + acc_row(r, lane), col = 32 * w + l32;
+    cur[r] = 0.5f * st[row * kD + col];
+    S[acc_row(r, lane)][col] = cur[r];
   }
+  store(dir == 0 ? 0 : frames, cur);
+  store(dst_of(0), cur);                       // frame of step 0 is an anchor
   __syncthreads();
-  for (int step = 0; step < frames; ++step) {
-    const int t = dir == 0 ? step : frames - 1 - step;      // frame absorbed now
-    const int dst = dir == 0 ? t + 1 : t;                   // state index written
-    float* so = states + (size_t)dst * kMat;
-    if (t >= 1 && t <= frames - 2) {
-      const float* pm = P + ((size_t)h * frames + t) * kMat;
-      const float* cm = C + ((size_t)h * frames + t) * kMat;
-      f32x16 acc;
+  f32x4 pa[16], pb[16];
+  f32x16 ca, cb;
+  auto load = [&](int t, f32x4 (&pt)[16], f32x16& c) {
+    const size_t m = (size_t)h * frames + t;
+    const f32x4* src = (const f32x4*)(PT + m * kMat + (32 * w + l32) * kD + 64 * half);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = cm[(32 * rt + acc_row(r, lane)) * kD + 32 * ct + l32];
-#pragma unroll 8
-      for (int s2 = 0; s2 < kD; s2 += 2)
-        acc = mfma(S[32 * rt + l32][s2 + half], pm[(s2 + half) * kD + 32 * ct + l32], acc);
-      __syncthreads();   // every wave has read the old state
+    for (int j = 0; j < 16; ++j) pt[j] = src[j];
+    const float* cm = C + m * kMat + 32 * w + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[32 * rt + acc_row(r, lane)][32 * ct + l32] = acc[r];
-      __syncthreads();
-    }
-    for (int i = i0; i < kD; i += 8) so[i * kD + j0] = S[i][j0];
+    for (int r = 0; r < 16; ++r) c[r] = cm[(32 * rb + acc_row(r, lane)) * kD];
+  };
+  auto step = [&](int i, const f32x4 (&pt)[16], const f32x16& c, f32x4 (&pt_next)[16], f32x16& c_next) {
+    if (i + 1 <= frames - 2) load(frame_of(i + 1), pt_next, c_next);
+    f32x16 acc = c;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) acc = mfma(S[l32][64 * half + k], pt[k >> 2][k & 3], acc);
+    __syncthreads();   // every wave has read the old band
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[acc_row(r, lane)][32 * w + l32] = acc[r];
+    __syncthreads();
+    cur = acc;
+    store(dst_of(i), cur);
+  };
+  if (frames > 2) load(frame_of(1), pa, ca);
+  for (int i = 1; i <= frames - 2; i += 2) {
+    step(i, pa, ca, pb, cb);
+    if (i + 1 <= frames - 2) step(i + 1, pb, cb, pa, ca);
   }
+  if (frames > 1) store(dst_of(frames - 1), cur);   // the other anchor
 }
 
 // out rows of frame f: o = (fwd[lo] + rev[hi]) q on the bf16 matrix cores.  q is
@@ -458,8 +482,8 @@ hipError_t launch_vda_states(const uint16_t* k, const uint16_t* v, const float* 
     hipLaunchKernelGGL(vda_inverse_kernel, grid, dim3(256), 0, stream, A, alpha, frames, M, P);
     hipLaunchKernelGGL(vda_matmul_kernel, grid, dim3(256), 0, stream, B, M, frames, C);
   }
-  hipLaunchKernelGGL(vda_scan_kernel, dim3(heads, 2), dim3(1024), 0, stream, P, C, s_text, frames, fwd,
-                     rev);
+  hipLaunchKernelGGL(vda_scan_kernel, dim3(4, heads, 2), dim3(256), 0, stream, P, C, s_text, frames,
+                     fwd, rev);
   return hipGetLastError();
 }
 
