@@ -388,9 +388,11 @@ void vda_scan_kernel(const float* __restrict__ PT, const float* __restrict__ C,
 // out rows of frame f: o = (fwd[lo] + rev[hi]) q on the bf16 matrix cores.  q is
 // bf16 already; W = fwd[lo] + rev[hi] is split into W_hi = bf16(W) and W_lo =
 // bf16(W - W_hi), |W - W_hi - W_lo| <= 2^-18 |W|, and o = W_hi q + W_lo q with
-// fp32 accumulation.  In the transposed product O^T = W Q^T both operands are
+// fp32 accumulation.  In the product O = Q W^T both operands are
 // row-contiguous: lane l of v_mfma_f32_32x32x16_bf16 takes 8 consecutive head
-// dims of row l % 32 of W (from LDS) and of query l % 32 (from global).  One
+// dims of query l % 32 (A, from global) and of row l % 32 of W (B, from LDS),
+// and each output register of a half-wave is 32 consecutive head dims of one
+// query, so every store instruction writes two whole 128-byte segments.  One
 // workgroup per (frame, head); wave w covers query tiles w, w + 4, ...
 constexpr int kWPitch = kD + 8;   // bf16 row pitch of the staged W halves: 16-byte chunks rotate per row
 
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __rest
   const int ntiles = (ft + 31) / 32;
   for (int nt = w; nt < ntiles; nt += 4) {
     const int qrow = 32 * nt + l32;
-    // B operand: query qrow, dims 16 kt + 8 g + 0..7 (rows past ft read zeros)
+    // A operand: query qrow, dims 16 kt + 8 g + 0..7 (rows past ft read zeros)
     bf16x8 qb[8];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
@@ -447,16 +449,14 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __rest
       for (int kt = 0; kt < 8; ++kt) {
         const bf16x8 ah = *(const bf16x8*)&w_hi[32 * mt + l32][16 * kt + 8 * g];
         const bf16x8 al = *(const bf16x8*)&w_lo[32 * mt + l32][16 * kt + 8 * g];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qb[kt], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qb[kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[kt], ah, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[kt], al, acc, 0, 0, 0);
       }
-      // acc[4 j + i]: head dim 32 mt + 8 j + 4 g + i of query qrow
-      if (qrow < ft) {
+      // acc[r]: query 32 nt + acc_row(r, lane), head dim 32 mt + l32
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v4 = {acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
-          *(f32x4*)(of + (size_t)qrow * kD + 32 * mt + 8 * j + 4 * g) = v4;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * nt + acc_row(r, lane);
+        if (row < ft) of[(size_t)row * kD + 32 * mt + l32] = acc[r];
       }
     }
   }
