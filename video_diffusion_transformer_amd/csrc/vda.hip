@@ -393,13 +393,13 @@ void vda_scan_kernel(const float* __restrict__ PT, const float* __restrict__ C,
 // dims of query l % 32 (A, from global) and of row l % 32 of W (B, from LDS),
 // and each output register of a half-wave is 32 consecutive head dims of one
 // query, so every store instruction writes two whole 128-byte segments.  One
-// workgroup per (frame, head); wave w covers query tiles w, w + 4, ...
+// eight-wave workgroup per (frame, head); wave w covers query tiles w, w + 8, ...
 constexpr int kWPitch = kD + 8;   // bf16 row pitch of the staged W halves: 16-byte chunks rotate per row
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(512) void vda_readout_kernel(const uint16_t* __restrict__ Q,
                                                           const float* __restrict__ fwd,
                                                           const float* __restrict__ rev, int ft,
                                                           int frames, int chunk, int nb,
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __rest
   }
   const float* wf = fwd + ((size_t)h * (frames + 1) + lo) * kMat;
   const float* wr = rev + ((size_t)h * (frames + 1) + hi) * kMat;
-  for (int x = tid; x < kMat; x += 256) {
+  for (int x = tid; x < kMat; x += 512) {
     const int i = x >> 7, j = x & (kD - 1);
     const float wv = wf[x] + wr[x];
     const __bf16 h16 = (__bf16)wv;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qf), (short)0, ft * kD * 2, 0x00020000);
   const int ntiles = (ft + 31) / 32;
-  for (int nt = w; nt < ntiles; nt += 4) {
+  for (int nt = w; nt < ntiles; nt += 8) {
     const int qrow = 32 * nt + l32;
     // A operand: query qrow, dims 16 kt + 8 g + 0..7 (rows past ft read zeros)
     bf16x8 qb[8];
@@ -490,7 +490,7 @@ hipError_t launch_vda_states(const uint16_t* k, const uint16_t* v, const float* 
 hipError_t launch_vda_readout(const uint16_t* q, const float* fwd, const float* rev, int heads,
                               int frames, int ft, int chunk, int nb, float* out, hipStream_t stream) {
   if (heads <= 0 || frames <= 0) return hipSuccess;
-  hipLaunchKernelGGL(vda_readout_kernel, dim3(frames, heads), dim3(256), 0, stream, q, fwd, rev, ft,
+  hipLaunchKernelGGL(vda_readout_kernel, dim3(frames, heads), dim3(512), 0, stream, q, fwd, rev, ft,
                      frames, chunk, nb, out);
   return hipGetLastError();
 }
