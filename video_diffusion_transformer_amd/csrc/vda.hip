@@ -293,8 +293,11 @@ void vda_inverse_kernel(const float* __restrict__ A, const float* __restrict__ a
   }
 }
 
-// out[b] = X[b] Y[b] for the interior frames' 128 x 128 matrices, b = h * frames
-// + t.  Wave w owns row tile w.
+// C_t = B_t M_t for the interior frames (b = h * frames + t).  M_t is symmetric,
+// so column j of M_t is row j: wave w computes column band w of C_t and holds
+// M_t[32 w + l32][64 g .. 64 g + 63] (k = 64 g + i in product i, g the lane
+// half) in registers from 16 vector loads; B_t is staged in LDS for the A
+// operands of all four row tiles.
 __global__ __launch_bounds__(256) void vda_matmul_kernel(const float* __restrict__ X,
                                                          const float* __restrict__ Y, int frames,
                                                          float* __restrict__ out) {
@@ -302,21 +305,23 @@ __global__ __launch_bounds__(256) void vda_matmul_kernel(const float* __restrict
   const size_t b = (size_t)blockIdx.y * frames + blockIdx.x + 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
   const float* x = X + b * kMat;
-  const float* y = Y + b * kMat;
+  const f32x4* yrow = (const f32x4*)(Y + b * kMat + (32 * w + l32) * kD + 64 * half);
+  f32x4 yv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) yv[j] = yrow[j];
   for (int i = tid >> 7; i < kD; i += 2) xs[i][tid & (kD - 1)] = x[i * kD + (tid & (kD - 1))];
   __syncthreads();
-  f32x16 acc[4];
+  float* o = out + b * kMat + 32 * w + l32;
+#pragma unroll 1
+  for (int I = 0; I < 4; ++I) {
+    f32x16 acc;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < kD; s += 2) {
-    const float av = xs[32 * w + l32][s + half];
+    for (int k = 0; k < 64; ++k) acc = mfma(xs[32 * I + l32][64 * half + k], yv[k >> 2][k & 3], acc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = mfma(av, y[(s + half) * kD + 32 * j + l32], acc[j]);
+    for (int r = 0; r < 16; ++r) o[(32 * I + acc_row(r, lane)) * kD] = acc[r];
   }
-  store_row_tile(out + b * kMat, w, acc, lane);
 }
 
 // The scans: S_t = S_prev P_t + C_t over the interior frames, forward from
