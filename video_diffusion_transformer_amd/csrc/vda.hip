@@ -74,7 +74,7 @@ constexpr int kTileB = kChunk * kD * 2;  // bytes of one chunk tile
 
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
-__global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void vda_stats_kernel(const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
                                                         const float* __restrict__ beta, int ft,
                                                         int frames, float* __restrict__ A,
@@ -111,24 +111,36 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { acc_a[j][r] = 0.f; acc_b[j][r] = 0.f; }
-  for (int u0 = 0; u0 < ft; u0 += kChunk) {
-    __syncthreads();   // the previous chunk has been consumed
-    // stage: 64 tokens x 16 chunks of 8 dims, 4 per thread
+  // raw K, V and beta of a chunk, 64 tokens x 16 chunks of 8 dims, 4 per
+  // thread; the next chunk's loads are in flight while this one is multiplied
+  u32x4s kw[4], vw[4];
+  float bw[4];
+  auto fetch = [&](int u0) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int pos = tid + 256 * x, row = pos >> 4, c = pos & 15;
       const int u = u0 + row;
-      u32x4s kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      float b = 0.f;
+      kw[x] = u32x4s{0u, 0u, 0u, 0u};
+      vw[x] = u32x4s{0u, 0u, 0u, 0u};
+      bw[x] = 0.f;
       if (u < ft) {
-        kw = *(const u32x4s*)(K + (tok0 + u) * kD + 8 * c);
-        vw = *(const u32x4s*)(V + (tok0 + u) * kD + 8 * c);
-        b = beta[tok0 + u];
+        kw[x] = *(const u32x4s*)(K + (tok0 + u) * kD + 8 * c);
+        vw[x] = *(const u32x4s*)(V + (tok0 + u) * kD + 8 * c);
+        bw[x] = beta[tok0 + u];
       }
+    }
+  };
+  fetch(0);
+  for (int u0 = 0; u0 < ft; u0 += kChunk) {
+    __syncthreads();   // the previous chunk has been consumed
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int pos = tid + 256 * x, row = pos >> 4, c = pos & 15;
+      const float b = bw[x];
       bf16x8s xh, xl, yh, yl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t kk = kw[e >> 1], vv = vw[e >> 1];
+        const uint32_t kk = kw[x][e >> 1], vv = vw[x][e >> 1];
         const float kf = __uint_as_float((e & 1) ? (kk & 0xffff0000u) : (kk << 16));
         const float vf = __uint_as_float((e & 1) ? (vv & 0xffff0000u) : (vv << 16));
         const float xk = b * kf, yv = b * vf;
@@ -138,13 +150,14 @@ __global__ __launch_bounds__(256) void vda_stats_kernel(const uint16_t* __restri
         yl[e] = (__bf16)(yv - (float)yh[e]);
       }
       const int off = row * kD * 2 + ((c ^ v_swz(row)) << 4);
-      *(u32x4s*)(lds[0] + off) = kw;
+      *(u32x4s*)(lds[0] + off) = kw[x];
       *(bf16x8s*)(lds[1] + off) = xh;
       *(bf16x8s*)(lds[2] + off) = xl;
       *(bf16x8s*)(lds[3] + off) = yh;
       *(bf16x8s*)(lds[4] + off) = yl;
     }
     __syncthreads();
+    if (u0 + kChunk < ft) fetch(u0 + kChunk);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bf16x8s xh = frag(1, w, st), xl = frag(2, w, st), yh = frag(3, w, st), yl = frag(4, w, st);
