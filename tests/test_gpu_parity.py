@@ -378,7 +378,8 @@ def test_vda_states_match_oracle(frames, ft):
         assert_close_rel(rev[h].cpu().numpy(), rr, f"vda rev states F={frames} ft={ft} h={h}")
 
 
-@pytest.mark.parametrize("frames,ft,chunk,nb", [(7, 64, 2, 1), (12, 100, 3, 1), (20, 64, 5, 1), (9, 130, 3, 0)])
+@pytest.mark.parametrize("frames,ft,chunk,nb", [(1, 5, 5, 1), (2, 64, 5, 1), (3, 64, 1, 0), (7, 64, 2, 1),
+                                                 (12, 100, 3, 1), (20, 64, 5, 1), (9, 130, 3, 0)])
 def test_vda_readout_matches_oracle(frames, ft, chunk, nb):
     say("vda readout", frames, ft, chunk, nb)
     (q, k, v, beta, alpha, s_text), wide = _vda_case(frames, ft, 2, 950 + frames)
