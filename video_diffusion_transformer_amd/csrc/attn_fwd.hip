@@ -762,8 +762,8 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     attn_fwd_kernel<1, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         q, k, v, out, idx, keep, tokens, qtiles, c, ListParams{});
   } else {
-    // 256 query rows per workgroup (8 waves) share each K/V stage; one
-    // workgroup per CU leaves LDS for three slots, loads two stages ahead
+    // 256 query rows per workgroup (8 waves) share each K/V stage (two LDS
+    // slots each for K and V); one workgroup per CU, two waves per SIMD
     const int qtiles = (tokens + 255) / 256;
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
