@@ -370,7 +370,7 @@ def main():
         pass
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attn_fwd_kernel<0, 8, 2, 1, 64> (dense)",
+                "traffic": traffic, "kernel": "attn_fwd_kernel<0, 4, 2, 1, 64> (dense)",
                 "avg_launch_ms": round(dense_launch_ms, 4)}
 
     result = {

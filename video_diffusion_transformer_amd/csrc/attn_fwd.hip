@@ -12,9 +12,9 @@
 // DeltaNet comes in", for the window).
 //
 // Design (one workgroup = one head x kBM query rows, one wave per 32 rows;
-// dense and window: 8 waves, 256 rows, one workgroup per CU; sparse: 4 waves,
-// 128 rows = one selection tile, two workgroups per CU; either way two waves
-// per SIMD with 256 registers each):
+// dense and sparse: 4 waves, 128 rows (for sparse one selection tile), two
+// workgroups per CU; window, INT8 and VSA-H3: 8 waves, 256 rows, one
+// workgroup per CU; either way two waves per SIMD with 256 registers each):
 // * Both products run on the bf16 matrix cores, v_mfma_f32_32x32x16_bf16, in
 //   transposed form: S^T = K Q^T (A = K from LDS, B = Q^T held in registers for
 //   the whole kernel) and O^T = V^T P^T (A = V^T from LDS, B = P^T taken
@@ -32,7 +32,8 @@
 //   past the sequence end.  K and V are stored row-major with XOR swizzles on
 //   16-byte chunks (each lane fetches the global chunk that belongs at its LDS
 //   slot); the V^T operand is read with the gfx950 LDS transpose load
-//   ds_read_b64_tr_b16.  Each slot is its own LDS array and the stage waits
+//   ds_read_b64_tr_b16, two operands ahead of the MFMA that takes them.
+//   Each slot is its own LDS array and the stage waits
 //   are explicit vmcnt counts before a bare barrier, so no LDS read waits for
 //   loads it does not consume.
 // * Software pipeline per stage j: the S^T MFMAs of stage j+1 run while the
@@ -73,6 +74,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kRowBytes = kHeadDim * 2;     // 256 B per token row
 constexpr int kXcds = 8;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+// LDS operand reads issued ahead of the MFMA that consumes them (two cover
+// the read latency better than one; more gains nothing measurable).
+constexpr int kReadAhead = 2;
 constexpr int kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
 // s_waitcnt immediates: vmcnt in bits 3:0, expcnt 6:4 (7 = no wait), lgkmcnt
 // 11:8.  kWaitVm(n) waits until at most n buffer loads are in flight and every
@@ -613,13 +617,14 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     qk(Buf<kSlotK>(), Snext);
     // Region 1: one K-operand read per (dk, kb) feeds kQB MFMAs; the softmax's
     // ~56 kQB kKB VALU instructions are spread between the MFMAs.  Reads run
-    // one operand ahead.
+    // kReadAhead operands ahead.
     {
       constexpr int kOps = kDK * kKB, kValuPerMfma = (56 * kKB * kQB + kOps * kQB - 1) / (kOps * kQB);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int o = 0; o < kReadAhead; ++o) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
-        if (o + 1 < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (o + kReadAhead < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -645,13 +650,14 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     rowmax(Snext, mx, cm_next);
     // Region 2: two transpose reads per (db, st) V operand feed kQB MFMAs; the
     // row max of the next stage (and in INT8 mode the conversion of its
-    // scores) fills the gaps.  Reads run one operand ahead.
+    // scores) fills the gaps.  Reads run kReadAhead operands ahead.
     {
       constexpr int kOps = 4 * 2 * kKB, kValu = kI8 ? 4 : 2;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+      for (int o = 0; o < kReadAhead; ++o) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
-        if (o + 1 < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        if (o + kReadAhead < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
@@ -762,12 +768,14 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     attn_fwd_kernel<1, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         q, k, v, out, idx, keep, tokens, qtiles, c, ListParams{});
   } else {
-    // 256 query rows per workgroup (8 waves) share each K/V stage (two LDS
-    // slots each for K and V); one workgroup per CU, two waves per SIMD
-    const int qtiles = (tokens + 255) / 256;
+    // 128 query rows per workgroup (4 waves) share each K/V stage (two LDS
+    // slots each for K and V); two workgroups per CU, so the two waves of a
+    // SIMD belong to different workgroups and never wait at each other's
+    // stage barrier (2-3% faster than one 8-wave workgroup of 256 rows)
+    const int qtiles = (tokens + 127) / 128;
     const long long blocks = (long long)heads * qtiles;
     if (blocks <= 0) return hipSuccess;
-    attn_fwd_kernel<0, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+    attn_fwd_kernel<0, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         q, k, v, out, idx, keep, tokens, qtiles, c, ListParams{});
   }
   return hipGetLastError();
