@@ -532,7 +532,7 @@ int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, i
   if (rc != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const int keep = keep_of(g.tiles, keep_frac);
-  const int blocks = (g.npad + 255) / 256, nsub = g.npad / 64;
+  const int blocks = (g.npad + fvattn::kVsaRows - 1) / fvattn::kVsaRows, nsub = g.npad / 64;
   const size_t packed = align256(sizeof(uint16_t) * (size_t)heads * g.npad * kHeadDim);
   const size_t means = align256(sizeof(double) * (size_t)heads * g.tiles * kHeadDim);
   const size_t idxb = align256(sizeof(int32_t) * (size_t)heads * g.tiles * keep);

@@ -159,7 +159,8 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   static_assert(!kI8 || (kBN == 64 && kStages == 2), "INT8 scales are per 64-key stage, loaded one stage ahead");
   constexpr int kPrefetch = kStages - 1;
   static_assert(kMode != 1 || kBM == kTile, "per-head lists cover one selection tile");
-  static_assert(kMode != 3 || (kBN == 64 && kBM == 256), "VSA entries are 64-key stages of 256-row blocks");
+  static_assert(kMode != 3 || (kBN == 64 && kBM == kVsaRows),
+                "VSA entries are 64-key stages of kVsaRows-row blocks");
   // One LDS array per slot: distinct objects let the compiler see that a read
   // of one slot cannot alias a buffer-to-LDS load still landing in another,
   // so it does not wait for every load in flight before each LDS read.
@@ -811,13 +812,14 @@ hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uin
 hipError_t launch_attention_vsa(const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
                                 uint16_t* out, const int32_t* lists, const ListParams& lp,
                                 int heads, float scale, hipStream_t stream) {
-  // the dense shape: 256 padded query slots per workgroup (8 waves), one list
-  // of 64-key sub-tiles per (head, block)
+  // kVsaRows padded query slots per workgroup (one wave per 32), one list of
+  // 64-key sub-tiles per (head, block)
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  const int qtiles = (lp.vsa.npad + 255) / 256;
+  const int qtiles = (lp.vsa.npad + kVsaRows - 1) / kVsaRows;
   const long long blocks = (long long)heads * qtiles;
   if (blocks <= 0) return hipSuccess;
-  attn_fwd_kernel<3, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+  attn_fwd_kernel<3, kVsaRows / 32, 2, 1, 64>
+      <<<dim3((unsigned)blocks), dim3(2 * kVsaRows), 0, stream>>>(
       q, kp, vp, out, lists, 0, lp.vsa.npad, qtiles, c, lp);
   return hipGetLastError();
 }

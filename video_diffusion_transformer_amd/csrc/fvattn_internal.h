@@ -71,6 +71,9 @@ __host__ __device__ inline int vsa_sub_count(const VsaGeom& g, int s) {
 // keys - 1, 22-25 the 64-row query groups of the block that attend to it, and
 // kMaskFlag when some group does not or some key is padding.
 constexpr int kVsaCountShift = 16, kVsaGroupShift = 22;
+// Query rows per VSA-H3 attention workgroup and per key list: a multiple of
+// 64 (one group per 64 rows, at most four groups), one wave per 32 rows.
+constexpr int kVsaRows = 128;
 
 // Per-launch parameters of the list-driven modes.  Frame window: latent
 // frames of frame_tokens tokens, chunks of chunk_frames frames, `neighbours`
@@ -127,7 +130,7 @@ hipError_t launch_vsa_pack(const uint16_t* k, const uint16_t* v, uint16_t* kp, u
 hipError_t launch_vsa_means(const uint16_t* x, double* out, const VsaGeom& g, int heads,
                             bool transposed, hipStream_t stream);
 
-// VSA-H3: per (head, 256-row query block) the ascending list of 64-key
+// VSA-H3: per (head, kVsaRows-row query block) the ascending list of 64-key
 // sub-tiles its rows attend to, from the kept video tiles idx [heads][tiles][keep]:
 // lists [heads][blocks][npad / 64], counts [heads][blocks].
 hipError_t launch_vsa_lists(const int32_t* idx, int keep, const VsaGeom& g, int heads,

@@ -13,7 +13,7 @@
 //   caller's layout; the sum walks the tile's tokens in (t, h, w) raster order
 //   from +0.0, then one correctly rounded division by the tile's token count.
 //   Scores and top-k then run in select.hip over the video tiles only.
-// * vsa_lists_kernel: per head and 256-row query block, the ascending list of
+// * vsa_lists_kernel: per head and kVsaRows-row query block, the ascending list of
 //   64-key sub-tiles that some query of the block attends to: every non-empty
 //   sub-tile for a block of non-video queries; the non-video sub-tiles plus
 //   the sub-tiles of the kept video tiles for a block of video queries.  Each
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(256) void vsa_lists_kernel(const int32_t* __restric
   for (int s = tid; s < nsub; s += 256) member[s] = 0;
   __syncthreads();
   int groups = 0;   // query groups of this block that hold slots (uniform)
-  for (int grp = 0; grp < 4; ++grp) {
-    const int row0 = 256 * b + 64 * grp;
+  for (int grp = 0; grp < kVsaRows / 64; ++grp) {
+    const int row0 = kVsaRows * b + 64 * grp;
     if (row0 >= g.npad) break;
     groups |= 1 << grp;
     const uint8_t bit = (uint8_t)(1 << grp);
@@ -188,7 +188,7 @@ hipError_t launch_vsa_means(const uint16_t* x, double* out, const VsaGeom& g, in
 
 hipError_t launch_vsa_lists(const int32_t* idx, int keep, const VsaGeom& g, int heads,
                             int32_t* lists, int32_t* counts, hipStream_t stream) {
-  const int blocks = (g.npad + 255) / 256;
+  const int blocks = (g.npad + kVsaRows - 1) / kVsaRows;
   if (heads <= 0 || blocks <= 0) return hipSuccess;
   if (g.npad / 64 > kMaxSub) return hipErrorInvalidValue;
   hipLaunchKernelGGL(vsa_lists_kernel, dim3(blocks, heads), dim3(256), 0, stream, idx, keep, g,
