@@ -12,8 +12,8 @@
 // DeltaNet comes in", for the window).
 //
 // Design (one workgroup = one head x kBM query rows, one wave per 32 rows;
-// dense and sparse: 4 waves, 128 rows (for sparse one selection tile), two
-// workgroups per CU; window, INT8 and VSA-H3: 8 waves, 256 rows, one
+// dense, sparse, window and VSA-H3: 4 waves, 128 rows (for sparse one
+// selection tile), two workgroups per CU; INT8: 8 waves, 256 rows, one
 // workgroup per CU; either way two waves per SIMD with 256 registers each):
 // * Both products run on the bf16 matrix cores, v_mfma_f32_32x32x16_bf16, in
 //   transposed form: S^T = K Q^T (A = K from LDS, B = Q^T held in registers for
@@ -785,13 +785,14 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
 hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    uint16_t* out, const int32_t* idx, const ListParams& wp,
                                    int heads, int tokens, float scale, hipStream_t stream) {
-  // the dense shape: 256 query rows per workgroup (8 waves); idx and
-  // wp.counts hold one list per 256-row block (kWindowRows)
+  // kWindowRows query rows per workgroup (one wave per 32); idx and
+  // wp.counts hold one list per kWindowRows-row block
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
   const int qtiles = (tokens + kWindowRows - 1) / kWindowRows;
   const long long blocks = (long long)heads * qtiles;
   if (blocks <= 0) return hipSuccess;
-  attn_fwd_kernel<2, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+  attn_fwd_kernel<2, kWindowRows / 32, 2, 1, 64>
+      <<<dim3((unsigned)blocks), dim3(2 * kWindowRows), 0, stream>>>(
       q, k, v, out, idx, 0, tokens, qtiles, c, wp);
   return hipGetLastError();
 }

@@ -101,7 +101,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             float scale, hipStream_t stream);
 
 // Query rows per workgroup of the windowed softmax, and so per key-tile list.
-constexpr int kWindowRows = 256;
+constexpr int kWindowRows = 128;
 // Bit set in an internal window-list entry when the key tile needs
 // per-element masking for some row of the block (a disallowed frame, or keys
 // past the sequence end).

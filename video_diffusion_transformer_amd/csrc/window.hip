@@ -3,8 +3,8 @@
 // of latent frames sees its neighbouring chunks, and the first and last
 // frames see and are seen by every frame).
 //
-// One wave per block of q_rows query tokens (128 for the public lists, 256 for
-// the attention workgroups).  A key tile is listed when some query of the
+// One wave per block of q_rows query tokens (128, the tile size, for both the
+// public lists and the attention workgroups).  A key tile is listed when some query of the
 // block may attend to some key of it.  Frames inside a tile are contiguous
 // and chunks grow with frames, so this is a closed-form interval test: either
 // tile holds an anchor frame, or the chunk ranges of the two tiles lie within
