@@ -1,6 +1,7 @@
 // Fused attention forward for gfx950 (MI355X): dense, restricted to a list of
-// 128-token key tiles per 128-token query tile (block-sparse), or restricted
-// to a frame window (Video DeltaNet's softmax branch).
+// 128-token key tiles per 128-token query tile (block-sparse), restricted to a
+// frame window (Video DeltaNet's softmax branch), over VSA-H3's packed 3D-tile
+// layout, or dense with INT8 query-key scores.
 //
 // What it computes: out = softmax(scale * Q K^T) V per head, non-causal, the
 // softmax taken over every key (dense), over the keys of the listed tiles only
@@ -32,10 +33,10 @@
 //   past the sequence end.  K and V are stored row-major with XOR swizzles on
 //   16-byte chunks (each lane fetches the global chunk that belongs at its LDS
 //   slot); the V^T operand is read with the gfx950 LDS transpose load
-//   ds_read_b64_tr_b16, two operands ahead of the MFMA that takes them.
-//   Each slot is its own LDS array and the stage waits
-//   are explicit vmcnt counts before a bare barrier, so no LDS read waits for
-//   loads it does not consume.
+//   ds_read_b64_tr_b16; K and V operand reads run two MFMAs ahead of their
+//   use.  Each slot is its own LDS array and the stage waits are explicit
+//   vmcnt counts before a bare barrier, so no LDS read waits for loads it does
+//   not consume.
 // * Software pipeline per stage j: the S^T MFMAs of stage j+1 run while the
 //   softmax of stage j (exp2, row sums, bf16 packing) runs on the vector ALU;
 //   then the PV MFMAs of stage j run while the row max of stage j+1 is taken.
@@ -800,7 +801,8 @@ hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const u
 hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
                                  uint16_t* out, const ListParams& lp, int heads, int tokens,
                                  float scale, hipStream_t stream) {
-  // the dense shape: 256 query rows per workgroup (8 waves), 64-key stages
+  // 256 query rows per workgroup (8 waves; 4-wave workgroups measured no
+  // gain for this mode), 64-key stages
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
   const int qtiles = (tokens + 255) / 256;
   const long long blocks = (long long)heads * qtiles;
