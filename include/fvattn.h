@@ -107,7 +107,7 @@ typedef enum { FVATTN_DENSE = 0, FVATTN_BLOCK_SPARSE = 1, FVATTN_DENSE_INT8QK = 
 int fvattn_keep_count(int tokens, double keep_frac);
 
 /* Attention forward for `heads` heads of `tokens` tokens (see the header
- * comment for the two modes).  q, k, v: bf16 [heads][tokens][head_dim] in;
+ * comment for the three modes).  q, k, v: bf16 [heads][tokens][head_dim] in;
  * out: bf16 [heads][tokens][head_dim] out (every row written).  scale
  * multiplies QK^T (1/sqrt(128) for H3-shaped heads).  keep_frac is used in
  * FVATTN_BLOCK_SPARSE mode only. */
@@ -150,7 +150,7 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
  * frames with 1 neighbour on each side give the page's 15-frame window).
  * q, k, v, out as in fvattn_forward.  frame_tokens >= 64 (else
  * FVATTN_ERR_UNSUPPORTED), chunk_frames >= 1, neighbours >= 0.  Uses
- * stream-ordered scratch for the key-tile lists (ceil(tokens/256) * (T + 1)
+ * stream-ordered scratch for the key-tile lists (ceil(tokens/128) * (T + 1)
  * int32). */
 int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
                           int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,

@@ -1,9 +1,10 @@
 // C ABI of the video-token attention library (declared in include/fvattn.h).
 //
 // Host side only: argument checks (all of them before any HIP call), the
-// keep count of compute_topk, stream-ordered scratch for the sparse, window and
-// VSA-H3 modes, and the head-group loop.  Every step of the computation runs
-// in the kernels of attn_fwd.hip, select.hip, window.hip and vsa.hip.
+// keep count of compute_topk, stream-ordered scratch for the sparse, INT8,
+// window, VSA-H3 and Video Delta Attention paths, and the head-group loop.
+// Every step of the computation runs in the kernels of attn_fwd.hip,
+// select.hip, quant.hip, window.hip, vsa.hip and vda.hip.
 
 #include <math.h>
 #include <stdlib.h>
