@@ -174,6 +174,27 @@ def test_select_ties_exact_on_tile_constant_inputs():
 
 # ------------------------------------------------------------------ sparse
 
+# Tile counts that need the three widest row-select variants (22, 28 and 32
+# slots of 64 scores per lane): 1,400 tiles with a ragged last tile, 1,750, and
+# 2,048, the largest sparse sequence (262,144 tokens).  Selection compared in
+# full, attention on sampled rows.
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("N", [1400 * 128 - 37, 1750 * 128, 2048 * 128])
+def test_select_and_sparse_at_large_tile_counts(N):
+    say("large tile count", N)
+    q, k, v = inputs.make_qkv(N, 1, "frame", 70 + N % 97)
+    qd, kd, vd = to_dev(q, k, v)
+    idx = fv.select_tiles(qd, kd, keep_frac=0.1).cpu().numpy()
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    ref = oracle.select_tiles(qw, kw, 0.1)
+    assert idx.shape == ref.shape
+    assert np.array_equal(idx, ref)
+    out = fv.forward(qd, kd, vd, mode="sparse", keep_frac=0.1).cpu()
+    rows = sample_rows(N, 16, N)
+    ref_out = oracle.sparse(qw, kw, vw, 1.0 / math.sqrt(128), idx, rows=rows)
+    assert_close(oracle.widen(out[:, rows]), ref_out, f"sparse at {N} tokens")
+
+
 @pytest.mark.parametrize("N,keep", [(300, 1), (300, 2), (1008, 3), (1000, 8), (2080, 5), (129, 1)])
 def test_forward_indexed_matches_oracle(N, keep):
     say("indexed", N, keep)
