@@ -238,6 +238,28 @@ def main():
                 rl_ms.append(rl_ev[0].elapsed_time(rl_ev[1]))
         del qg, kg, vg, og
 
+    # the matrix-core rate this GPU sustains right now (dependency-free MFMA
+    # loop), to read the roofline figure against besides the data-sheet peak
+    mfma_loop = None
+    if do_roofline:
+        sink = torch.empty(fv.PROBE_SINK, dtype=torch.float32, device=dev)
+        fv.mfma_probe(20000, sink)
+        torch.cuda.synchronize()
+        iters = 400000
+        p_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        p_ev[0].record(stream)
+        fv.mfma_probe(iters, sink)
+        p_ev[1].record(stream)
+        torch.cuda.synchronize()
+        pm = p_ev[0].elapsed_time(p_ev[1])
+        if not bool(torch.isfinite(sink).all()):
+            raise RuntimeError("MFMA probe produced non-finite sums")
+        mfma_loop = {"tflops": round(fv.PROBE_FLOP_PER_ITER * iters / (pm * 1e-3) / 1e12, 2),
+                     "ms": round(pm, 3),
+                     "what": "bf16 v_mfma_f32_32x32x16 chains, 4 per wave, 4 waves per SIMD, no memory "
+                             "traffic, run right after the roofline launches"}
+        del sink
+
     # split of the sparse time: selection alone, outside the timed region
     sel_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     idx_buf = torch.empty((GROUP, fv.tile_count(TOKENS), fv.keep_count(TOKENS, KEEP_FRAC)),
@@ -386,10 +408,12 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
+    loop_tf = mfma_loop["tflops"] if mfma_loop else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_fwd_kernel<0, 4, 2, 1, 64> (dense, one 16-head launch)",
-                "flop_per_launch": flop_launch, "avg_launch_ms": round(dense_launch_ms, 4)}
+                "flop_per_launch": flop_launch, "avg_launch_ms": round(dense_launch_ms, 4),
+                "frac_of_mfma_loop": round(achieved / loop_tf, 4) if loop_tf else None}
 
     result = {
         "metric": "attn TFLOP/s + % bf16 MFMA peak, 72,576 tok x 56 heads, dense & 90% sparse",
@@ -409,12 +433,14 @@ def main():
                    "tokens": TOKENS, "heads": HEADS, "head_dim": 128, "group_heads": GROUP,
                    "keep_frac": KEEP_FRAC, "seed": SEED},
         "dense": {"ms": round(d_ms, 3), "tflops": round(dense_tflops, 2),
-                  "frac_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4), "flop": flop_dense},
+                  "frac_peak": round(dense_tflops / PEAK_BF16_TFLOPS, 4), "flop": flop_dense,
+                  "frac_of_mfma_loop": round(dense_tflops / loop_tf, 4) if loop_tf else None},
         "sparse": {"ms": round(s_ms, 3), "tflops_effective": round(sparse_tflops, 2),
                    "frac_peak": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "flop": flop_sparse,
                    "selection_ms": round(float(np.median(sel_ms)), 3),
                    "speedup_vs_dense": round(d_ms / s_ms, 3) if do_dense and do_sparse else None},
         "roofline": roofline,
+        "mfma_loop": mfma_loop,
     }
     if window is not None:
         if do_dense:

@@ -252,6 +252,17 @@ int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double
 int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles, int head_dim,
                        double* scores_out, void* stream);
 
+/* Matrix-core rate probe, for reading the attention figures against what this
+ * GPU sustains at its present clock rather than against the data-sheet peak
+ * (2.5 PFLOP/s dense bf16 at 2.4 GHz): 4,096 waves each run `iters`
+ * iterations of four independent v_mfma_f32_32x32x16_bf16 chains, no memory
+ * traffic, i.e. 4096 * iters * 4 * 32768 FLOP; time the call with events on
+ * `stream`.  sink: float device buffer of at least FVATTN_PROBE_SINK floats
+ * (one sum per thread, written so the loop cannot be removed).
+ * INVALID_ARG for a NULL sink, sink_floats < FVATTN_PROBE_SINK or iters < 1. */
+#define FVATTN_PROBE_SINK 262144
+int fvattn_mfma_probe(float* sink, int sink_floats, int iters, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* fvattn_status_string(int status);
 

@@ -101,6 +101,12 @@ def test_forward_rejects_bad_arguments(lib, kw, want):
     assert _fwd(lib, **kw) == want
 
 
+@pytest.mark.parametrize("sink,floats,iters", [(NULL, fv.PROBE_SINK, 10), (BOGUS, fv.PROBE_SINK - 1, 10),
+                                               (BOGUS, fv.PROBE_SINK, 0), (BOGUS, 0, 10)])
+def test_mfma_probe_rejects_bad_arguments(lib, sink, floats, iters):
+    assert lib.fvattn_mfma_probe(sink, floats, iters, NULL) == fv.FVATTN_ERR_INVALID_ARG
+
+
 def test_dense_ignores_keep_frac_checks(lib):
     # keep_frac is not looked at in dense mode: a bad one plus a NULL pointer
     # still reports the pointer

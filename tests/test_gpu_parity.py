@@ -240,6 +240,16 @@ def test_head_groups_equal_one_launch_bitwise():
             assert torch.equal(whole, grouped), (mode, g)
 
 
+def test_mfma_probe_runs_every_iteration():
+    # the sums grow linearly with the iteration count (exact: small dyadic
+    # operands), so a loop cut short or dropped would show
+    a = fv.mfma_probe(64).clone()
+    b = fv.mfma_probe(128).clone()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(a).all()) and float(a.abs().sum()) > 0
+    assert torch.equal(b, 2 * a)
+
+
 # ------------------------------------------------------------------ frame window (Video DeltaNet's softmax branch)
 
 @pytest.mark.parametrize("N,ft,chunk,nb", [(1, 64, 5, 1), (64, 64, 5, 1), (1000, 64, 2, 1), (900, 100, 3, 1),

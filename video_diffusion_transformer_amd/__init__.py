@@ -27,6 +27,9 @@ FVATTN_DENSE_INT8QK = 2
 TILE = 128
 HEAD_DIM = 128
 MAX_TILES = 2048
+PROBE_SINK = 262144
+PROBE_WAVES = 4096
+PROBE_FLOP_PER_ITER = PROBE_WAVES * 4 * 32768
 
 _MODES = {"dense": FVATTN_DENSE, "sparse": FVATTN_BLOCK_SPARSE, "int8": FVATTN_DENSE_INT8QK,
           FVATTN_DENSE: FVATTN_DENSE, FVATTN_BLOCK_SPARSE: FVATTN_BLOCK_SPARSE,
@@ -52,6 +55,7 @@ SIGNATURES = {
     "fvattn_quantize_k": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "fvattn_vda_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fvattn_vda_states": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "fvattn_mfma_probe": (_I, [_P, _I, _I, _P]),
     "fvattn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -341,3 +345,17 @@ def vda_states(k, v, beta, alpha, s_text, frame_tokens: int, stream=None):
         _check(load().fvattn_vda_states(_ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(s_text), H, F,
                                         int(frame_tokens), d, _ptr(fwd), _ptr(rev), _stream_ptr(stream)))
     return fwd, rev
+
+
+def mfma_probe(iters: int, sink=None, stream=None):
+    """fvattn_mfma_probe: PROBE_FLOP_PER_ITER * iters FLOP of bf16 MFMAs on the
+    current device; returns the float32 sink (time the call with events)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(PROBE_SINK, dtype=torch.float32, device="cuda")
+    if sink.dtype != torch.float32 or not sink.is_cuda or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 device tensor")
+    with torch.cuda.device(sink.device):
+        _check(load().fvattn_mfma_probe(_ptr(sink), min(sink.numel(), 2**31 - 1), int(iters),
+                                         _stream_ptr(stream)))
+    return sink

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfvattn.so")
-SOURCES = ["attn_fwd.hip", "select.hip", "window.hip", "vsa.hip", "quant.hip", "vda.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "select.hip", "window.hip", "vsa.hip", "quant.hip", "vda.hip", "probe.hip",
+           "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

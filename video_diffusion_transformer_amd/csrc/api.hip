@@ -4,7 +4,8 @@
 // keep count of compute_topk, stream-ordered scratch for the sparse, INT8,
 // window, VSA-H3 and Video Delta Attention paths, and the head-group loop.
 // Every step of the computation runs in the kernels of attn_fwd.hip,
-// select.hip, quant.hip, window.hip, vsa.hip and vda.hip.
+// select.hip, quant.hip, window.hip, vsa.hip and vda.hip (probe.hip: the
+// matrix-core rate probe used to read the measurements).
 
 #include <math.h>
 #include <stdlib.h>
@@ -571,6 +572,14 @@ int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, i
   rc = hip_status(e);
   const int rf = hip_status(hipFreeAsync(base, st));
   return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_mfma_probe(float* sink, int sink_floats, int iters, void* stream) {
+  if (!sink || sink_floats < FVATTN_PROBE_SINK || iters < 1) return FVATTN_ERR_INVALID_ARG;
+  static_assert(fvattn::kProbeBlocks * 256 == FVATTN_PROBE_SINK, "one float per probe thread");
+  int rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  return hip_status(fvattn::launch_mfma_probe(sink, iters, (hipStream_t)stream));
 }
 
 const char* fvattn_status_string(int status) {

@@ -182,6 +182,12 @@ hipError_t launch_scores(const double* qm, const double* kmT, int heads, int til
 hipError_t launch_select(const double* scores, int heads, int tiles, int keep, int32_t* idx_out,
                          hipStream_t stream);
 
+// Matrix-core rate probe: kProbeBlocks workgroups of 256 threads, each wave
+// `iters` iterations of four bf16 32x32x16 MFMAs; one float per thread into
+// sink (kProbeBlocks * 256 floats).
+constexpr int kProbeBlocks = 1024;
+hipError_t launch_mfma_probe(float* sink, int iters, hipStream_t stream);
+
 // [heads][T][128] -> [heads][128][T] (fp64), for the score diagnostic entry.
 hipError_t launch_transpose_means(const double* in, double* out, int heads, int tiles,
                                   hipStream_t stream);
