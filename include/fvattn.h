@@ -56,6 +56,11 @@
  * Stream: `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call only enqueues work and returns; no host
  *   synchronization happens inside.
+ * Graph capture: dense-mode fvattn_forward and fvattn_forward_heads and
+ *   fvattn_forward_indexed allocate nothing and enqueue only kernels, so a
+ *   caller can capture them into a HIP graph and replay it (after one call
+ *   outside capture, which caches the device check).  The other entry points
+ *   allocate stream-ordered scratch inside the call.
  * Bounds: nothing is read or written past `tokens`; a partial last tile is
  *   masked (its missing keys get -inf scores, its missing query rows are never
  *   stored).

@@ -240,6 +240,42 @@ def test_head_groups_equal_one_launch_bitwise():
             assert torch.equal(whole, grouped), (mode, g)
 
 
+def test_allocation_free_paths_replay_in_a_graph():
+    # dense attention, the head-group launcher in dense mode and sparse
+    # attention from caller lists allocate nothing, so they can be captured
+    # into a graph; every replay, with eager work and synchronizations in
+    # between, must reproduce the eager result bit for bit
+    q, k, v = to_dev(*inputs.make_qkv(1500, 6, "frame", 72))
+    idx = fv.select_tiles(q, k, keep_frac=0.25)
+    want = [fv.forward(q, k, v), fv.forward_heads(q, k, v, 4), fv.forward_indexed(q, k, v, idx)]
+    outs = [torch.empty_like(q) for _ in want]
+
+    def run():
+        fv.forward(q, k, v, out=outs[0])
+        fv.forward_heads(q, k, v, 4, out=outs[1])
+        fv.forward_indexed(q, k, v, idx, out=outs[2])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        scratch = (q.float() * (rep + 1)).sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, o, w in zip(("dense", "heads", "indexed"), outs, want):
+            assert torch.equal(o, w), (rep, name)
+        del scratch
+
+
 def test_mfma_probe_runs_every_iteration():
     # the sums grow linearly with the iteration count (exact: small dyadic
     # operands), so a loop cut short or dropped would show
