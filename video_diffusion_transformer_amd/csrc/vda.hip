@@ -13,10 +13,13 @@
 // frame f reads o = fwd[lo(f)] q + rev[hi(f)] q, lo / hi the frames just
 // before and after its softmax window (both seeds for the anchor frames).
 //
-// Every product is fp32 on the matrix cores (v_mfma_f32_32x32x2_f32: lane l
-// holds A[l % 32][l / 32] and B[l / 32][l % 32]); the inverse is an in-place
-// Gauss-Jordan elimination held in the matrix-core accumulators, which needs
-// no pivoting because I + A_t is symmetric with eigenvalues >= 1.
+// Every product runs on the matrix cores at fp32 accuracy.  Where one operand
+// is bf16 already (k, v, q), the fp32 operand is split into bf16 hi + lo parts
+// and the two products run on the bf16 MFMA with fp32 accumulation (A_t, B_t
+// and the readout); the rest uses v_mfma_f32_32x32x2_f32 (lane l holds
+// A[l % 32][l / 32] and B[l / 32][l % 32]).  The inverse is a Gauss-Jordan
+// elimination held in the matrix-core accumulators, which needs no pivoting
+// because I + A_t is symmetric with eigenvalues >= 1.
 //
 // Kernels: vda_stats_kernel (A_t, B_t per frame), vda_inverse_kernel (M_t and
 // P_t^T), vda_matmul_kernel (C_t = B_t M_t), vda_scan_kernel (one workgroup per
