@@ -567,6 +567,44 @@ def test_vsa_full_size(vsa72, tile):
     assert_close(oracle.widen(got), ref, f"vsa full size {tile}")
 
 
+@pytest.mark.timeout(300)
+def test_vsa_near_the_tile_limit():
+    # 1,980 video tiles of (4, 4, 4) (the limit is 2,048) behind a 700-token
+    # prefix: the widest row select, the longest per-block key lists
+    prefix, grid, tile, frac = 700, (120, 24, 42), (4, 4, 4), 0.1
+    q, k, v = _vsa_inputs(prefix, grid, 1, 9)
+    qd, kd, vd = to_dev(q, k, v)
+    assert fv.vsa_tile_count(grid, tile) == 1980
+    idx = fv.vsa_select(qd, kd, prefix, grid, tile, frac).cpu().numpy()
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    ref_idx = oracle.vsa_select(qw, kw, prefix, grid, tile, frac)
+    assert np.array_equal(idx, ref_idx)
+    out = fv.forward_vsa(qd, kd, vd, prefix, grid, tile, frac)
+    N = q.shape[1]
+    rng = np.random.default_rng(12)
+    rows = sorted(set([0, prefix - 1, prefix, prefix + 1, N - 1] + rng.integers(0, N, 16).tolist()))
+    ref = oracle.vsa_attention(qw, kw, vw, 1 / math.sqrt(128), prefix, grid, tile, frac, rows=rows,
+                               idx=ref_idx)
+    assert_close(oracle.widen(out[:, rows].cpu()), ref, "vsa near the tile limit")
+
+
+@pytest.mark.parametrize("mode", ["dense", "sparse", "int8"])
+def test_many_heads_short_sequences(mode):
+    # 96 heads of 200 tokens: a grid of many small heads with ragged tiles
+    q, k, v = inputs.make_qkv(200, 96, "iid", 13)
+    out = fv.forward(*to_dev(q, k, v), mode=mode, keep_frac=0.5).cpu()
+    heads = [0, 1, 47, 95]
+    qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
+    scale = 1 / math.sqrt(128)
+    if mode == "dense":
+        ref = oracle.dense(qw, kw, vw, scale)
+    elif mode == "sparse":
+        ref = oracle.sparse(qw, kw, vw, scale, oracle.select_tiles(qw, kw, 0.5))
+    else:
+        ref = oracle.int8_scores_attention(qw, kw, vw, scale)
+    assert_close(oracle.widen(out[heads]), ref, f"{mode} 96 heads x 200")
+
+
 @pytest.mark.timeout(400)
 def test_config4_int8(cfg4):
     c = inputs.CONFIGS[4]
