@@ -93,9 +93,12 @@ def cpu_baseline(q, k, v, scale, budget_s: float):
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas_threads = 1
+    affinity = len(os.sched_getaffinity(0))
+    # the oracle's parallel work is its BLAS calls; the rest is one thread
+    threads = max(1, min(blas_threads, affinity))
     qw, kw, vw = (oracle.widen(t[:1]) for t in (q, k, v))
     t0 = time.perf_counter()
     idx = oracle.select_tiles(qw, kw, KEEP_FRAC)
@@ -117,6 +120,7 @@ def cpu_baseline(q, k, v, scale, budget_s: float):
     value = flop / elapsed / 1e12
     return {
         "value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "affinity_cores": affinity, "blas_threads": blas_threads,
         "sample": (f"fp64 numpy oracle, head 0 of {HEADS}: tile selection over all {T} tiles "
                    f"({t_sel:.1f} s), then dense and 90%-sparse attention for query tiles 0-{tiles - 1} "
                    f"({tiles * 128} rows), {elapsed:.1f} s in total; effective FLOP of those rows / time"),

@@ -52,7 +52,12 @@
  * Ownership: the caller owns every buffer and the stream.  The library never
  *   frees caller memory.  Sparse mode allocates its scratch (tile means, the
  *   fp64 tile score matrix [heads][T][T] and index lists) stream-ordered on
- *   the caller's stream and releases it there.
+ *   the caller's stream and releases it there.  Scratch comes from a memory
+ *   pool the library creates per device on its first call there (release
+ *   threshold: keep everything, so repeated calls do not return to the
+ *   driver); the pool lives until the process ends and holds at most the
+ *   largest scratch that calls overlapping in stream order have needed.  The
+ *   device's default memory pool is not touched.
  * Stream: `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call only enqueues work and returns; no host
  *   synchronization happens inside.
@@ -72,8 +77,11 @@
  *                             keep_frac that is NaN or outside (0, 1] (sparse
  *                             only; ignored in dense mode), keep outside [1, T].
  *     FVATTN_ERR_UNSUPPORTED  head_dim != 128, group_heads not in {16, 8, 4},
- *                             sparse mode with T > FVATTN_MAX_TILES, a tensor
- *                             with 2^31 or more elements, or a current device
+ *                             sparse mode with T > FVATTN_MAX_TILES, one
+ *                             head's slice of a tensor with 2^31 or more
+ *                             elements (tokens > 16,777,215 at head_dim 128;
+ *                             larger head counts are fine, heads are
+ *                             addressed in 64 bits), or a current device
  *                             that is not gfx950.
  *     FVATTN_ERR_ALLOC        a stream-ordered scratch allocation failed.
  *     FVATTN_ERR_HIP          a HIP call or kernel launch reported an error.
@@ -234,7 +242,13 @@ int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t
  * [heads][frames * frame_tokens][128].  All device pointers.  Products and
  * the inverse run in fp32 (matrix cores, Gauss-Jordan without pivoting on the
  * symmetric I + A_t, eigenvalues >= 1 for beta >= 0).  Uses stream-ordered
- * scratch of (5 * heads * frames + 2 * heads * (frames + 1)) * 64 KiB. */
+ * scratch of (5 * heads * frames + 2 * heads * (frames + 1)) * 64 KiB.
+ * PRECONDITION: every beta is finite and >= 0 (the page's write weights).
+ * The values live on the device and are not checked: a negative beta can
+ * make I + A_t singular or indefinite, where the unpivoted elimination has
+ * no guarantee, and a NaN or infinite beta propagates; the output is then
+ * undefined (no fault, but no meaningful numbers).  UNSUPPORTED also for
+ * frame_tokens > 8,388,607 (one frame's bf16 rows reach 2^31 bytes). */
 int fvattn_vda_forward(const void* q, const void* k, const void* v, const float* beta,
                        const float* alpha, const float* s_text, float* out, int heads, int frames,
                        int frame_tokens, int head_dim, int chunk_frames, int neighbours,
@@ -242,7 +256,8 @@ int fvattn_vda_forward(const void* q, const void* k, const void* v, const float*
 
 /* The two scans of fvattn_vda_forward alone: fwd_out, rev_out float
  * [heads][frames + 1][128][128]; fwd[t] has absorbed the written frames
- * before t, rev[t] those from t on; fwd[0] = rev[frames] = s_text / 2. */
+ * before t, rev[t] those from t on; fwd[0] = rev[frames] = s_text / 2.
+ * Same PRECONDITION as fvattn_vda_forward: every beta finite and >= 0. */
 int fvattn_vda_states(const void* k, const void* v, const float* beta, const float* alpha,
                       const float* s_text, int heads, int frames, int frame_tokens, int head_dim,
                       float* fwd_out, float* rev_out, void* stream);

@@ -314,3 +314,63 @@ def test_vda_argument_checks(lib, monkeypatch):
     monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
     assert fw(*args(), NULL) == fv.FVATTN_ERR_ALLOC
     assert st(BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, 2, 7, 64, 128, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_ALLOC
+
+
+def test_vda_frame_size_limit(lib):
+    fw = lib.fvattn_vda_forward
+    # one frame's bf16 rows must stay below 2^31 bytes (8,388,608 x 256 B is 2^31)
+    assert fw(BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, 1, 1, 8388608, 128, 5, 1,
+              NULL) == fv.FVATTN_ERR_UNSUPPORTED
+
+
+def test_token_limit_is_per_head_elements(lib):
+    # one head's tensor must hold fewer than 2^31 elements: 2^24 tokens x 128 is 2^31
+    for mode in (0, 1, 2):
+        assert _fwd(lib, heads=1, tokens=1 << 24, mode=mode) == fv.FVATTN_ERR_UNSUPPORTED
+    assert lib.fvattn_forward_indexed(BOGUS, BOGUS, BOGUS, BOGUS, 1, BOGUS, 1, 1 << 24, 128, 0.088,
+                                      NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    # 2^23 tokens (2^31 bytes of one head) pass the argument checks; without a
+    # GPU the call then fails at the device check, not at the size check
+    assert _fwd(lib, heads=1, tokens=1 << 23, mode=0) == fv.FVATTN_ERR_HIP
+
+
+@pytest.mark.parametrize("tokens,rows,count,stride,ok", [
+    (72576, 128, 567, 567, True),        # the layout the window entry point allocates
+    (72576, 128, 600, 700, True),        # more room than needed
+    (72576, 256, 567, 567, False),       # lists built for another block height
+    (72576, 128, 566, 567, False),       # one list short
+    (72576, 128, 567, 566, False),       # rows too narrow for every key tile
+    (1, 128, 1, 1, True),
+    (129, 128, 1, 2, False),
+])
+def test_window_list_layout_check(lib, tokens, rows, count, stride, ok):
+    fn = lib.fvattn_internal_window_lists_fit
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int] * 4
+    want = fv.FVATTN_OK if ok else fv.FVATTN_ERR_INVALID_ARG
+    assert fn(tokens, rows, count, stride) == want
+
+
+def test_vda_binding_checks_shapes_before_use():
+    H, F, ft = 2, 3, 8
+    N = F * ft
+    bf, f32 = torch.bfloat16, torch.float32
+    good = dict(q=torch.zeros(H, N, 128, dtype=bf), k=torch.zeros(H, N, 128, dtype=bf),
+                v=torch.zeros(H, N, 128, dtype=bf), beta=torch.zeros(H, N, dtype=f32),
+                alpha=torch.ones(H, F, 128, dtype=f32), s_text=torch.zeros(H, 128, 128, dtype=f32))
+    bad = [("beta", torch.zeros(H, N - 1, dtype=f32)), ("alpha", torch.ones(H, F + 1, 128, dtype=f32)),
+           ("s_text", torch.zeros(H, 128, 64, dtype=f32)), ("v", torch.zeros(H, N, 128, dtype=f32)),
+           ("beta", torch.zeros(H, 2 * N, dtype=f32)[:, ::2])]
+    for name, t in bad:
+        a = dict(good, **{name: t})
+        with pytest.raises(ValueError, match=name):
+            fv.vda_forward(a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["s_text"], ft)
+        with pytest.raises(ValueError, match=name):
+            fv.vda_states(a["k"], a["v"], a["beta"], a["alpha"], a["s_text"], ft)
+    with pytest.raises(ValueError, match="out"):
+        fv.vda_forward(*good.values(), ft, out=torch.zeros(H, N, 64, dtype=f32))
+    # right shapes on the CPU: refused as host tensors, before any library call
+    with pytest.raises(ValueError, match="device"):
+        fv.vda_forward(*good.values(), ft)
+    with pytest.raises(ValueError, match="frame"):
+        fv.vda_states(good["k"], good["v"], good["beta"], good["alpha"], good["s_text"], 7)

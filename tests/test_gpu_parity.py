@@ -8,6 +8,7 @@ in full.
 """
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -22,6 +23,12 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+# Relative Frobenius error of a bf16 output against the fp64 oracle: the
+# output's own bf16 rounding is ~0.2% and P rounded to bf16 before the PV
+# product adds about as much, so 1% leaves room for neither a dropped term
+# nor a systematic scale error (which the absolute bars can miss where
+# outputs are small: at 72,576 frame-correlated tokens mean |o| is ~0.03).
+REL_FRO = 1e-2
 DEV = "cuda:0"
 
 
@@ -33,13 +40,15 @@ def to_dev(*ts):
     return [t.to(DEV) for t in ts]
 
 
-def assert_close(got, ref, what=""):
+def assert_close(got, ref, what="", rel_max=REL_FRO):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref)
     mx, mean = float(err.max()), float(err.mean())
-    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref)) / nref if nref > 0 else float(np.linalg.norm(got))
     say(f"{what}: max_abs={mx:.3e} mean_abs={mean:.3e} rel_fro={rel:.3e}")
     assert mx <= MAX_ABS and mean <= MEAN_ABS, (what, mx, mean)
+    assert rel <= rel_max, (what, "rel_fro", rel)
 
 
 def sample_rows(N, n_random, seed):
@@ -527,6 +536,67 @@ def _full_size_window(cid, qkv):
     qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
     ref = oracle.window_attention(qw, kw, vw, c.scale, 1008, 5, 1, rows=rows)
     assert_close(oracle.widen(got), ref, f"{c.name} window")
+
+
+def _oracle_rows(fn, N, chunk=512, workers=16):
+    """fn(rows) for every row 0..N-1, chunks computed in parallel threads (one
+    BLAS thread each); concatenated along the row axis."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    chunks = [np.arange(a, min(a + chunk, N)) for a in range(0, N, chunk)]
+    workers = max(1, min(workers, len(os.sched_getaffinity(0))))
+    done = [0]
+
+    def run(r):
+        o = fn(r)
+        done[0] += 1
+        if done[0] % 32 == 0:
+            say(f"  oracle rows: {done[0]} of {len(chunks)} chunks")
+        return o
+
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(run, chunks))
+    return np.concatenate(parts, axis=1)
+
+
+def _full_head(cid, qkv, head, modes):
+    """Every row of one head at full size, for each mode, through the same
+    launches the bench makes (head groups for dense and sparse, one launch for
+    the window)."""
+    c = inputs.CONFIGS[cid]
+    q, k, v = qkv
+    qd, kd, vd = to_dev(q, k, v)
+    qw, kw, vw = (oracle.widen(t[head:head + 1]) for t in (q, k, v))
+    for mode in modes:
+        say(c.name, mode, "head", head, "every row")
+        if mode == "window":
+            out = fv.forward_window(qd, kd, vd, frame_tokens=1008, chunk_frames=5, neighbours=1,
+                                    scale=c.scale)
+            fn = lambda r: oracle.window_attention(qw, kw, vw, c.scale, 1008, 5, 1, rows=r)
+        elif mode == "sparse":
+            out = fv.forward_heads(qd, kd, vd, c.group, scale=c.scale, mode="sparse",
+                                   keep_frac=c.keep_frac)
+            idx = oracle.select_tiles(qw, kw, c.keep_frac)
+            fn = lambda r: oracle.sparse(qw, kw, vw, c.scale, idx, rows=r)
+        else:
+            out = fv.forward_heads(qd, kd, vd, c.group, scale=c.scale, mode="dense")
+            fn = lambda r: oracle.dense(qw, kw, vw, c.scale, rows=r)
+        got = out[head:head + 1].cpu()
+        del out
+        ref = _oracle_rows(fn, c.tokens)
+        assert_close(oracle.widen(got), ref, f"{c.name} {mode} head {head} all {c.tokens} rows")
+
+
+@pytest.mark.timeout(900)
+def test_config4_every_row_of_one_head(cfg4):
+    # head 55 is in the last (8-head) group of the launcher
+    _full_head(4, cfg4, 55, ("dense", "sparse", "window"))
+
+
+@pytest.mark.timeout(900)
+def test_config5_every_row_of_one_head(cfg5):
+    _full_head(5, cfg5, 0, ("sparse", "window", "dense"))
 
 
 @pytest.mark.timeout(300)

@@ -303,42 +303,59 @@ def quantize_k(k, stream=None):
     return codes, scales
 
 
-def _check_f32(*ts):
+def _check_vda(q, k, v, beta, alpha, s_text, frame_tokens: int, out=None):
+    """Shapes, dtypes, contiguity and device of the Video Delta Attention
+    tensors (q may be None for the states call); returns (H, N, F)."""
     torch = _torch()
-    for t in ts:
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("expected contiguous float32 device tensors")
+    ref = k
+    if ref.dim() != 3 or ref.shape[2] != HEAD_DIM:
+        raise ValueError("k must be [heads, tokens, 128]")
+    H, N, d = ref.shape
+    ft = int(frame_tokens)
+    if ft <= 0 or N % ft:
+        raise ValueError("tokens must be frames * frame_tokens")
+    F = N // ft
+    want = [(k, (H, N, d), torch.bfloat16, "k"), (v, (H, N, d), torch.bfloat16, "v"),
+            (beta, (H, N), torch.float32, "beta"), (alpha, (H, F, d), torch.float32, "alpha"),
+            (s_text, (H, d, d), torch.float32, "s_text")]
+    if q is not None:
+        want.insert(0, (q, (H, N, d), torch.bfloat16, "q"))
+    if out is not None:
+        want.append((out, (H, N, d), torch.float32, "out"))
+    for t, shape, dtype, name in want:
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for t, _, _, name in want:
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"{name} must be a device tensor on the device of k")
+    return H, N, F
 
 
 def vda_forward(q, k, v, beta, alpha, s_text, frame_tokens: int, chunk_frames: int = 5,
                 neighbours: int = 1, out=None, stream=None):
-    """fvattn_vda_forward: Video Delta Attention readout, float32 [heads, tokens, 128]."""
+    """fvattn_vda_forward: Video Delta Attention readout, float32 [heads, tokens, 128].
+    Precondition (not checked on the device): every beta finite and >= 0."""
     torch = _torch()
-    H, N, d = _check_qkv(q, k, v)
-    F = N // int(frame_tokens)
-    if F * int(frame_tokens) != N:
-        raise ValueError("tokens must be frames * frame_tokens")
-    _check_f32(beta, alpha, s_text)
-    if tuple(beta.shape) != (H, N) or tuple(alpha.shape) != (H, F, d) or tuple(s_text.shape) != (H, d, d):
-        raise ValueError("beta [H, N], alpha [H, F, 128], s_text [H, 128, 128] expected")
+    H, N, F = _check_vda(q, k, v, beta, alpha, s_text, frame_tokens, out)
     if out is None:
-        out = torch.empty((H, N, d), dtype=torch.float32, device=q.device)
-    _check_f32(out)
+        out = torch.empty((H, N, HEAD_DIM), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         _check(load().fvattn_vda_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
-                                         _ptr(s_text), _ptr(out), H, F, int(frame_tokens), d,
+                                         _ptr(s_text), _ptr(out), H, F, int(frame_tokens), HEAD_DIM,
                                          int(chunk_frames), int(neighbours), _stream_ptr(stream)))
     return out
 
 
 def vda_states(k, v, beta, alpha, s_text, frame_tokens: int, stream=None):
-    """fvattn_vda_states: (fwd, rev) float32 [heads, frames + 1, 128, 128]."""
+    """fvattn_vda_states: (fwd, rev) float32 [heads, frames + 1, 128, 128].
+    Precondition (not checked on the device): every beta finite and >= 0."""
     torch = _torch()
-    H, N, d = _check_qkv(k, v)
-    F = N // int(frame_tokens)
-    if F * int(frame_tokens) != N:
-        raise ValueError("tokens must be frames * frame_tokens")
-    _check_f32(beta, alpha, s_text)
+    H, N, F = _check_vda(None, k, v, beta, alpha, s_text, frame_tokens)
+    d = HEAD_DIM
     fwd = torch.empty((H, F + 1, d, d), dtype=torch.float32, device=k.device)
     rev = torch.empty_like(fwd)
     with torch.cuda.device(k.device):

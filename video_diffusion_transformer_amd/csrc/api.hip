@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdint>
 
 #include "../../include/fvattn.h"
@@ -39,22 +40,40 @@ int keep_of(int tiles, double keep_frac) {
   return want < 1.0 ? 1 : (int)want;
 }
 
+// Library-owned stream-ordered memory pool of each device (created on first
+// use, never destroyed): freed scratch stays in it between calls, and the
+// device's default pool, which other code in the process may use, is left
+// with its own settings.
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[kMaxDevices];
+
 int check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return FVATTN_ERR_UNSUPPORTED;
   int st = g_device_state[dev].load(std::memory_order_acquire);
   if (st == 0) {
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    st = g_device_state[dev].load(std::memory_order_acquire);
+    if (st != 0) return st == 1 ? FVATTN_OK : FVATTN_ERR_UNSUPPORTED;
     hipDeviceProp_t p;
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FVATTN_ERR_HIP;
     st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     if (st == 1) {
-      // keep freed stream-ordered scratch in the pool between calls
-      hipMemPool_t pool;
-      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-        uint64_t threshold = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+      hipMemPoolProps props;
+      memset(&props, 0, sizeof(props));
+      props.allocType = hipMemAllocationTypePinned;
+      props.handleTypes = hipMemHandleTypeNone;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      hipMemPool_t pool = nullptr;
+      if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+        (void)hipGetLastError();
+        return FVATTN_ERR_HIP;
       }
+      uint64_t threshold = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+      g_pools[dev] = pool;
     }
     g_device_state[dev].store(st, std::memory_order_release);
   }
@@ -67,6 +86,22 @@ bool test_fail_alloc() {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FVATTN_OK : FVATTN_ERR_HIP; }
+
+// Stream-ordered scratch from the current device's library pool (the device
+// has passed check_device); release with hipFreeAsync on the same stream.
+int scratch_malloc(void** p, size_t bytes, hipStream_t stream) {
+  *p = nullptr;
+  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices || !g_pools[dev])
+    return FVATTN_ERR_HIP;
+  if (hipMallocFromPoolAsync(p, bytes, g_pools[dev], stream) != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return FVATTN_ERR_ALLOC;
+  }
+  return FVATTN_OK;
+}
 
 // Scratch of one sparse call: tile means of Q [H][T][128], transposed tile
 // means of K [H][128][T], the tile scores [H][T][T], and the kept tile lists
@@ -86,12 +121,8 @@ int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_id
   const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
   const size_t scoreb = align256(sizeof(double) * (size_t)heads * tiles * tiles);
   const size_t idxb = need_idx ? align256(sizeof(int32_t) * (size_t)heads * tiles * keep) : 0;
-  if (test_fail_alloc()) return FVATTN_ERR_ALLOC;
-  if (hipMallocAsync(&s->base, 2 * means + scoreb + idxb, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    s->base = nullptr;
-    return FVATTN_ERR_ALLOC;
-  }
+  const int rc = scratch_malloc(&s->base, 2 * means + scoreb + idxb, stream);
+  if (rc != FVATTN_OK) return rc;
   char* p = (char*)s->base;
   s->qm = (double*)p;
   s->kmT = (double*)(p + means);
@@ -123,10 +154,8 @@ int forward_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16
   const size_t codeb = align256((size_t)heads * tokens * kHeadDim);
   const size_t scaleb = align256(sizeof(float) * (size_t)heads * nblk);
   void* base = nullptr;
-  if (test_fail_alloc() || hipMallocAsync(&base, codeb + scaleb, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  const int ra = scratch_malloc(&base, codeb + scaleb, stream);
+  if (ra != FVATTN_OK) return ra;
   uint8_t* codes = (uint8_t*)base;
   float* scales = (float*)((char*)base + codeb);
   hipError_t e = fvattn::launch_quantize_k(k, codes, scales, heads, tokens, stream);
@@ -221,8 +250,11 @@ int check_vsa_args(int heads, int tokens, int head_dim, int prefix, int frames, 
 int check_vda_args(int heads, int frames, int frame_tokens, int head_dim) {
   if (heads < 0 || frames < 0 || frame_tokens < 0) return FVATTN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
+  // one head's tensors below 2^31 elements; a frame's bf16 rows below 2^31
+  // bytes (the readout addresses a frame through one buffer descriptor)
   if ((long long)frames * frame_tokens * kHeadDim > kMaxPerHead ||
-      (long long)(frames + 1) * kHeadDim * kHeadDim > kMaxPerHead)
+      (long long)(frames + 1) * kHeadDim * kHeadDim > kMaxPerHead ||
+      (long long)frame_tokens * kHeadDim * 2 > kMaxPerHead)
     return FVATTN_ERR_UNSUPPORTED;
   return FVATTN_OK;
 }
@@ -345,11 +377,8 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   const int blocks = (tokens - 1) / fvattn::kWindowRows + 1;
   void* scratch = nullptr;
   const size_t idx_bytes = align256(sizeof(int32_t) * (size_t)blocks * T);
-  if (hipMallocAsync(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)blocks), st) !=
-      hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)blocks), st);
+  if (rc != FVATTN_OK) return rc;
   int32_t* idx = (int32_t*)scratch;
   int32_t* counts = (int32_t*)((char*)scratch + idx_bytes);
   fvattn::ListParams wp;
@@ -359,6 +388,11 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   wp.neighbours = neighbours;
   wp.frames = (tokens - 1) / frame_tokens + 1;
   wp.first_block = (int)((long long)(wp.frames - 1) * frame_tokens / fvattn::kWindowRows);
+  // the layout allocated above: launch_window_tiles writes `blocks` lists of
+  // kWindowRows rows, T entries apart; the attention launcher checks it again
+  wp.list_rows = fvattn::kWindowRows;
+  wp.list_count = blocks;
+  wp.list_stride = T;
   hipError_t e = fvattn::launch_window_tiles(tokens, wp, fvattn::kWindowRows, true, idx, counts, st);
   if (e == hipSuccess)
     e = fvattn::launch_attention_window((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
@@ -393,10 +427,8 @@ int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles,
   if (rc != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   void* kmT = nullptr;
-  if (hipMallocAsync(&kmT, sizeof(double) * (size_t)heads * tiles * kHeadDim, st) != hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&kmT, sizeof(double) * (size_t)heads * tiles * kHeadDim, st);
+  if (rc != FVATTN_OK) return rc;
   hipError_t e = fvattn::launch_transpose_means(km, (double*)kmT, heads, tiles, st);
   if (e == hipSuccess)
     e = fvattn::launch_scores(qm, (const double*)kmT, heads, tiles, scores_out, st);
@@ -432,10 +464,8 @@ int fvattn_vda_states(const void* k, const void* v, const float* beta, const flo
   hipStream_t st = (hipStream_t)stream;
   void* scratch = nullptr;
   const size_t bytes = sizeof(float) * 5 * (size_t)heads * frames * kHeadDim * kHeadDim;
-  if (hipMallocAsync(&scratch, bytes, st) != hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&scratch, bytes, st);
+  if (rc != FVATTN_OK) return rc;
   rc = hip_status(fvattn::launch_vda_states((const uint16_t*)k, (const uint16_t*)v, beta, alpha,
                                             s_text, heads, frames, frame_tokens, (float*)scratch,
                                             fwd_out, rev_out, st));
@@ -460,10 +490,8 @@ int fvattn_vda_forward(const void* q, const void* k, const void* v, const float*
   const size_t mat = (size_t)kHeadDim * kHeadDim;
   const size_t work = 5 * (size_t)heads * frames * mat, states = (size_t)heads * (frames + 1) * mat;
   void* scratch = nullptr;
-  if (hipMallocAsync(&scratch, sizeof(float) * (work + 2 * states), st) != hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&scratch, sizeof(float) * (work + 2 * states), st);
+  if (rc != FVATTN_OK) return rc;
   float* w = (float*)scratch;
   float* fwd = w + work;
   float* rev = fwd + states;
@@ -502,10 +530,8 @@ int fvattn_vsa_select(const void* q, const void* k, int heads, int tokens, int h
   const size_t means = align256(sizeof(double) * (size_t)heads * g.tiles * kHeadDim);
   const size_t scoreb = align256(sizeof(double) * (size_t)heads * g.tiles * g.tiles);
   void* base = nullptr;
-  if (hipMallocAsync(&base, 2 * means + scoreb, st) != hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&base, 2 * means + scoreb, st);
+  if (rc != FVATTN_OK) return rc;
   double* qm = (double*)base;
   double* kmT = (double*)((char*)base + means);
   double* scores = (double*)((char*)base + 2 * means);
@@ -542,11 +568,8 @@ int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, i
   const size_t cntb = align256(sizeof(int32_t) * (size_t)heads * blocks);
   const size_t scoreb = align256(sizeof(double) * (size_t)heads * g.tiles * g.tiles);
   void* base = nullptr;
-  if (hipMallocAsync(&base, 2 * packed + 2 * means + idxb + listb + cntb + scoreb, st) !=
-      hipSuccess) {
-    (void)hipGetLastError();
-    return FVATTN_ERR_ALLOC;
-  }
+  rc = scratch_malloc(&base, 2 * packed + 2 * means + idxb + listb + cntb + scoreb, st);
+  if (rc != FVATTN_OK) return rc;
   char* p = (char*)base;
   uint16_t* kp = (uint16_t*)p;
   uint16_t* vp = (uint16_t*)(p + packed);
@@ -580,6 +603,19 @@ int fvattn_mfma_probe(float* sink, int sink_floats, int iters, void* stream) {
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
   return hip_status(fvattn::launch_mfma_probe(sink, iters, (hipStream_t)stream));
+}
+
+// Not declared in the public header: the frame-window list-layout check of
+// the attention launcher, exposed so host tests can run it without a GPU.
+// Returns FVATTN_OK when `list_count` lists of `list_rows` rows, `list_stride`
+// entries apart, fit the window attention over `tokens` tokens, else
+// FVATTN_ERR_INVALID_ARG.
+int fvattn_internal_window_lists_fit(int tokens, int list_rows, int list_count, int list_stride) {
+  fvattn::ListParams wp;
+  wp.list_rows = list_rows;
+  wp.list_count = list_count;
+  wp.list_stride = list_stride;
+  return fvattn::window_lists_fit(tokens, wp) == hipSuccess ? FVATTN_OK : FVATTN_ERR_INVALID_ARG;
 }
 
 const char* fvattn_status_string(int status) {

@@ -112,8 +112,16 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes,
+// Buffer descriptor over `rows` rows of `row_bytes` bytes from `base` (fewer
+// than 1 row: an empty range).  The byte count is clamped to 2^31 - 1: every
+// access made through one descriptor lies within a few hundred KiB of its
+// base, so the clamp only keeps a long remaining range from overflowing the
+// 32-bit count (which would make it negative and read zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int rows,
+                                                            int row_bytes) {
+  const int cap = 0x7fffffff / row_bytes;
+  const int r = rows < 0 ? 0 : (rows > cap ? cap : rows);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, r * row_bytes,
                                            kBufferFlags);
 }
 
@@ -198,7 +206,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     // lane (row l32, half g) holds dims 32 dk + 16 g + 0..15 of its row; the
     // row's scale is max |q| / 127 over both halves; rows past N read zeros
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
+        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, N - q0, kRowBytes);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       u32x4 w[8];
@@ -239,7 +247,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   } else if constexpr (kMode == 3) {
     // gather: the lane's slot holds token vsa_slot_token(slot); padding reads
     // past the end of the descriptor and gets zeros
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, qn * kRowBytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, qn, kRowBytes);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int tok = vsa_slot_token(wp.vsa, q0 + 32 * qb + l32);
@@ -252,7 +260,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     }
   } else {
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, (N - q0) * kRowBytes);
+        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, N - q0, kRowBytes);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
@@ -265,7 +273,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 
   const int ktiles = (N + kTile - 1) / kTile;
   const int32_t* irow = kMode == 1   ? idx + ((size_t)h * qtiles + qt) * keep
-                        : kMode == 2 ? idx + (size_t)qt * ktiles
+                        : kMode == 2 ? idx + (size_t)qt * wp.list_stride
                         : kMode == 3 ? idx + ((size_t)h * qtiles + qt) * (N / kBN)
                                      : nullptr;
   const int nsub = kDenseWalk   ? (N + kBN - 1) / kBN
@@ -317,14 +325,14 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     voffg[i] = row * kRowBytes + ((slot ^ v_swz(row)) << 4);
   }
   auto load_k = [&](int kv0, auto bufc) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kKRowBytes, (N - kv0) * kKRowBytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * kKRowBytes, N - kv0, kKRowBytes);
     unsigned char* dst = k_slots[decltype(bufc)::value] + wave * kKLoadsPerWave * 1024;
 #pragma unroll
     for (int i = 0; i < kKLoadsPerWave; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, koffg[i], 0, 0, 0);
   };
   auto load_v = [&](int kv0, auto bufc) {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vh + (size_t)kv0 * kHeadDim, (N - kv0) * kRowBytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vh + (size_t)kv0 * kHeadDim, N - kv0, kRowBytes);
     unsigned char* dst = v_slots[decltype(bufc)::value] + wave * kLoadsPerWave * 1024;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
@@ -578,7 +586,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   // (loaded during stage it with a vector load, so the stage-top vmcnt wait
   // covers it).  Other modes: the multiplier is c throughout.
   const __amdgpu_buffer_rsrc_t rks =
-      make_rsrc(kI8 ? wp.kscale + (size_t)h * nsub : nullptr, kI8 ? nsub * 4 : 0);
+      make_rsrc(kI8 ? wp.kscale + (size_t)h * nsub : nullptr, kI8 ? nsub : 0, 4);
   auto key_scale = [&](int i) -> float {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4 * i, 0, 0));
   };
@@ -783,11 +791,22 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   return hipGetLastError();
 }
 
+hipError_t window_lists_fit(int tokens, const ListParams& wp) {
+  const int blocks = (tokens + kWindowRows - 1) / kWindowRows;
+  const int ktiles = (tokens + kTile - 1) / kTile;
+  if (tokens < 0 || wp.list_rows != kWindowRows || wp.list_count < blocks || wp.list_stride < ktiles)
+    return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
 hipError_t launch_attention_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    uint16_t* out, const int32_t* idx, const ListParams& wp,
                                    int heads, int tokens, float scale, hipStream_t stream) {
   // kWindowRows query rows per workgroup (one wave per 32); idx and
-  // wp.counts hold one list per kWindowRows-row block
+  // wp.counts hold one list per kWindowRows-row block, wp.list_stride entries
+  // apart; a list layout that does not match is refused before any launch
+  const hipError_t fit = window_lists_fit(tokens, wp);
+  if (fit != hipSuccess) return fit;
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
   const int qtiles = (tokens + kWindowRows - 1) / kWindowRows;
   const long long blocks = (long long)heads * qtiles;

@@ -92,7 +92,17 @@ struct ListParams {
   VsaGeom vsa;
   // INT8 query-key mode: per-64-key-block key scales [heads][ceil(N / 64)]
   const float* kscale = nullptr;
+  // Frame window: the geometry of the list array the caller allocated, rows
+  // per list (query rows one list covers), number of lists and int32 entries
+  // per list.  The launcher refuses a layout the kernel would index past.
+  int list_rows = 0, list_count = 0, list_stride = 0;
 };
+
+// hipSuccess when a frame-window list array of `wp` fits the attention
+// kernel over `tokens` tokens (kWindowRows rows per list, one list per
+// kWindowRows-row block, at least one entry per 128-token key tile per list),
+// hipErrorInvalidValue otherwise.  Host arithmetic only.
+hipError_t window_lists_fit(int tokens, const ListParams& wp);
 
 // Dense (idx == nullptr) or tile-list (idx != nullptr, `keep` entries per query
 // tile) attention forward over `heads` heads.

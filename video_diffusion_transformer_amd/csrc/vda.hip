@@ -450,6 +450,7 @@ __global__ __launch_bounds__(512) void vda_readout_kernel(const uint16_t* __rest
   const size_t N = (size_t)frames * ft;
   const uint16_t* qf = Q + ((size_t)h * N + (size_t)f * ft) * kD;
   float* of = out + ((size_t)h * N + (size_t)f * ft) * kD;
+  // ft * 256 < 2^31: the host rejects larger frames
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qf), (short)0, ft * kD * 2, 0x00020000);
   const int ntiles = (ft + 31) / 32;
