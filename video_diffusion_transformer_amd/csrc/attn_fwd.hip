@@ -113,16 +113,16 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 }
 
 // Buffer descriptor over `rows` rows of `row_bytes` bytes from `base` (fewer
-// than 1 row: an empty range).  The byte count is clamped to 2^31 - 1: every
-// access made through one descriptor lies within a few hundred KiB of its
-// base, so the clamp only keeps a long remaining range from overflowing the
-// 32-bit count (which would make it negative and read zeros).
+// than 1 row: an empty range).  The byte count is the descriptor's 32-bit
+// unsigned record count, formed in 64 bits: the host limits a head to fewer
+// than 2^24 rows of at most 256 bytes, so it stays below 2^32.  (Only a
+// lower clamp is applied: a min/max pair compiles to one vector med3, which
+// would put the descriptor in vector registers and wrap every load through
+// it in a readfirstlane loop.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int rows,
                                                             int row_bytes) {
-  const int cap = 0x7fffffff / row_bytes;
-  const int r = rows < 0 ? 0 : (rows > cap ? cap : rows);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, r * row_bytes,
-                                           kBufferFlags);
+  const long long bytes = rows > 0 ? (long long)rows * row_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
 }
 
 // Combine x with its value in the other half-wave (lane l and lane l ^ 32).
@@ -532,8 +532,12 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     }
   };
   // P = exp2(S c - m) as bf16 B-operands; P[qb][st] covers keys 32 kb + 16 g + 8 s + 0..7
-  // with st = 2 kb + s.
+  // with st = 2 kb + s.  The running sum adds the bf16 values of P, the ones
+  // the PV product multiplies, two at a time with v_dot2_f32_bf16 (half the
+  // vector instructions of adding the fp32 values one by one; 1% faster).
   auto softmax = [&](const f32x16 (&S)[kQB][kKB], bf16x8 (&P)[kQB][2 * kKB], const float (&cm)[kQB]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       float ps[2] = {0.f, 0.f};
@@ -542,8 +546,14 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = __builtin_amdgcn_exp2f(fmaf(S[qb][kb][r], cm[qb], -m_run[qb]));
-          ps[r & 1] += p;
           P[qb][2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        }
+#pragma unroll
+      for (int st = 0; st < 2 * kKB; ++st)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const bf16x2 pr = {P[qb][st][2 * w], P[qb][st][2 * w + 1]};
+          ps[w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[w & 1], false);
         }
       l_run[qb] += ps[0] + ps[1];
     }
