@@ -134,6 +134,26 @@ int fvattn_forward(const void* q, const void* k, const void* v, void* out, int h
 int fvattn_select_tiles(const void* q, const void* k, int heads, int tokens, int head_dim,
                         double keep_frac, int32_t* idx_out, void* stream);
 
+/* FVATTN_BLOCK_SPARSE attention of fvattn_forward (same kernels, same
+ * results bit for bit) that allocates nothing, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Its scratch (tile means, tile scores and kept
+ * lists) lives in one static device array of FVATTN_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends; the caller passes only inputs and outputs.
+ * Limit: 16 H T 128 + 8 H T^2 + 4 H T k bytes (each of the four parts rounded
+ * up to 256 bytes; T = ceil(tokens / 128), k the keep count) must fit in the
+ * array, else FVATTN_ERR_UNSUPPORTED before anything is enqueued (72,576
+ * tokens fit with 16 heads, 102,816 tokens with 8 heads).  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * Nothing in the array needs clearing between calls (every byte read is
+ * written first by the same call).  Other arguments and errors as
+ * fvattn_forward in FVATTN_BLOCK_SPARSE mode. */
+#define FVATTN_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int fvattn_forward_sparse_noalloc(const void* q, const void* k, const void* v, void* out,
+                                  int heads, int tokens, int head_dim, float scale,
+                                  double keep_frac, void* stream);
+
 /* Sparse attention from caller-given tile lists (the role of
  * block_sparse_attn_from_indices on the FastH3 page, section "What's actually
  * on the GPU: three kernels behind one switch").  idx: int32 [heads][T][keep]

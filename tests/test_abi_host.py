@@ -374,3 +374,25 @@ def test_vda_binding_checks_shapes_before_use():
         fv.vda_forward(*good.values(), ft)
     with pytest.raises(ValueError, match="frame"):
         fv.vda_states(good["k"], good["v"], good["beta"], good["alpha"], good["s_text"], 7)
+
+
+def _noalloc_bytes(heads, tokens, frac):
+    al = lambda n: (n + 255) // 256 * 256
+    T = oracle.tile_count(tokens)
+    k = oracle.keep_count(T, frac)
+    return 2 * al(8 * heads * T * 128) + al(8 * heads * T * T) + al(4 * heads * T * k)
+
+
+def test_noalloc_limit_is_checked_on_the_host(lib):
+    f = lib.fvattn_forward_sparse_noalloc
+    limit = 64 * 1024 * 1024
+    for heads, tokens in [(16, 72576), (8, 102816), (17, 72576), (9, 102816), (1, 262144), (64, 72576)]:
+        fits = _noalloc_bytes(heads, tokens, 0.1) <= limit
+        rc = f(BOGUS, BOGUS, BOGUS, BOGUS, heads, tokens, 128, 0.088, 0.1, NULL)
+        # within the limit the call goes on to the device check (no GPU here)
+        assert rc == (fv.FVATTN_ERR_HIP if fits else fv.FVATTN_ERR_UNSUPPORTED), (heads, tokens)
+    assert _noalloc_bytes(16, 72576, 0.1) <= limit and _noalloc_bytes(8, 102816, 0.1) <= limit
+    assert f(NULL, BOGUS, BOGUS, BOGUS, 1, 100, 128, 0.088, 0.1, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert f(BOGUS, BOGUS, BOGUS, BOGUS, 1, 100, 128, 0.088, 0.0, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert f(BOGUS, BOGUS, BOGUS, BOGUS, 1, 100, 64, 0.088, 0.1, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert f(NULL, NULL, NULL, NULL, 0, 100, 128, 0.088, 0.1, NULL) == fv.FVATTN_OK

@@ -44,6 +44,7 @@ SIGNATURES = {
     "fvattn_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _D, _P]),
     "fvattn_select_tiles": (_I, [_P, _P, _I, _I, _I, _D, _P, _P]),
     "fvattn_forward_indexed": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _F, _P]),
+    "fvattn_forward_sparse_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _D, _P]),
     "fvattn_forward_heads": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _D, _P]),
     "fvattn_tile_means": (_I, [_P, _I, _I, _I, _P, _P]),
     "fvattn_forward_window": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _P]),
@@ -150,6 +151,22 @@ def forward(q, k, v, scale: float | None = None, mode="dense", keep_frac: float 
     with torch.cuda.device(q.device):
         _check(load().fvattn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, N, d, scale,
                                      _MODES[mode], float(keep_frac), _stream_ptr(stream)))
+    return out
+
+
+def forward_sparse_noalloc(q, k, v, scale: float | None = None, keep_frac: float = 0.1, out=None,
+                           stream=None):
+    """fvattn_forward_sparse_noalloc: block-sparse attention with the library's static
+    scratch (no allocation inside the library; `out` may be passed in too)."""
+    torch = _torch()
+    H, N, d = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(load().fvattn_forward_sparse_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, N, d,
+                                                    scale, float(keep_frac), _stream_ptr(stream)))
     return out
 
 

@@ -47,6 +47,15 @@ int keep_of(int tiles, double keep_frac) {
 std::mutex g_pool_mutex;
 hipMemPool_t g_pools[kMaxDevices];
 
+// Scratch of fvattn_forward_sparse_noalloc: one array per GPU, in the code
+// object's device memory, for callers that cannot allocate.  Host code never
+// uses `scratch` itself (its host-side name is only a stand-in): it uses the
+// device address from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kStaticScratchBytes = FVATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
 int check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
@@ -116,19 +125,48 @@ struct SparseScratch {
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_idx,
-                  hipStream_t stream) {
+// Bytes of a sparse call's scratch, and its layout over `base`.
+size_t sparse_scratch_bytes(int heads, int tiles, int keep, bool need_idx) {
   const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
   const size_t scoreb = align256(sizeof(double) * (size_t)heads * tiles * tiles);
   const size_t idxb = need_idx ? align256(sizeof(int32_t) * (size_t)heads * tiles * keep) : 0;
-  const int rc = scratch_malloc(&s->base, 2 * means + scoreb + idxb, stream);
-  if (rc != FVATTN_OK) return rc;
-  char* p = (char*)s->base;
+  return 2 * means + scoreb + idxb;
+}
+
+void sparse_scratch_carve(SparseScratch* s, void* base, int heads, int tiles, bool need_idx) {
+  const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
+  const size_t scoreb = align256(sizeof(double) * (size_t)heads * tiles * tiles);
+  char* p = (char*)base;
   s->qm = (double*)p;
   s->kmT = (double*)(p + means);
   s->scores = (double*)(p + 2 * means);
   s->idx = need_idx ? (int32_t*)(p + 2 * means + scoreb) : nullptr;
+}
+
+int scratch_alloc(SparseScratch* s, int heads, int tiles, int keep, bool need_idx,
+                  hipStream_t stream) {
+  const int rc =
+      scratch_malloc(&s->base, sparse_scratch_bytes(heads, tiles, keep, need_idx), stream);
+  if (rc != FVATTN_OK) return rc;
+  sparse_scratch_carve(s, s->base, heads, tiles, need_idx);
   return FVATTN_OK;
+}
+
+// Device address of the current device's static scratch array, looked up
+// once per device with that device current; nullptr on failure.
+void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 int scratch_free(SparseScratch* s, hipStream_t stream) {
@@ -300,6 +338,30 @@ int fvattn_select_tiles(const void* q, const void* k, int heads, int tokens, int
   rc = run_selection((const uint16_t*)q, (const uint16_t*)k, heads, tokens, keep, s, idx_out, st);
   const int rf = scratch_free(&s, st);
   return rc != FVATTN_OK ? rc : rf;
+}
+
+int fvattn_forward_sparse_noalloc(const void* q, const void* k, const void* v, void* out,
+                                  int heads, int tokens, int head_dim, float scale,
+                                  double keep_frac, void* stream) {
+  bool empty;
+  int rc = check_forward_args(q, k, v, out, heads, tokens, head_dim, scale, FVATTN_BLOCK_SPARSE,
+                              keep_frac, &empty);
+  if (rc != FVATTN_OK || empty) return rc;
+  const int T = tiles_of(tokens);
+  const int keep = keep_of(T, keep_frac);
+  if (sparse_scratch_bytes(heads, T, keep, true) > kStaticScratchBytes) return FVATTN_ERR_UNSUPPORTED;
+  rc = check_device();
+  if (rc != FVATTN_OK) return rc;
+  void* base = static_scratch();
+  if (!base) return FVATTN_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  SparseScratch s;
+  sparse_scratch_carve(&s, base, heads, T, true);
+  const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k;
+  rc = run_selection(qq, kk, heads, tokens, keep, s, s.idx, st);
+  if (rc != FVATTN_OK) return rc;
+  return hip_status(fvattn::launch_attention(qq, kk, (const uint16_t*)v, (uint16_t*)out, s.idx,
+                                             keep, heads, tokens, scale, st));
 }
 
 int fvattn_forward_indexed(const void* q, const void* k, const void* v, const int32_t* idx,
