@@ -214,20 +214,36 @@ def window_frames_allowed(frames: int, chunk_frames: int = 5, neighbours: int = 
     return allowed
 
 
-def window_tiles(tokens: int, frame_tokens: int, chunk_frames: int = 5, neighbours: int = 1):
+def _window_token_frames(tokens: int, frame_tokens: int, prefix: int):
+    """Per token: -1 for the non-video prefix, else the latent frame of the
+    video token (counted from the first video token).  Returns (frames of
+    the video part, the per-token array)."""
+    video = tokens - prefix
+    frames = -(-video // frame_tokens)
+    tf = np.full(tokens, -1, dtype=np.int64)
+    tf[prefix:] = np.arange(video) // frame_tokens
+    return frames, tf
+
+
+def window_tiles(tokens: int, frame_tokens: int, chunk_frames: int = 5, neighbours: int = 1,
+                 prefix: int = 0):
     """Key tiles each 128-token query tile must visit: every key tile holding a
-    key that some query of the tile may attend to.  Returns (idx [T, T] int32,
-    padded with -1, ascending; count [T] int32)."""
+    key that some query of the tile may attend to.  With a non-video prefix
+    (text, audio) of ``prefix`` tokens ahead of the video, every prefix key is
+    visible to every query and a prefix query sees every key.  Returns (idx
+    [T, T] int32, padded with -1, ascending; count [T] int32)."""
     T = tile_count(tokens)
-    frames = -(-tokens // frame_tokens)
+    frames, token_frame = _window_token_frames(tokens, frame_tokens, prefix)
     allowed = window_frames_allowed(frames, chunk_frames, neighbours)
-    token_frame = np.arange(tokens) // frame_tokens
     idx = np.full((T, T), -1, dtype=np.int32)
     count = np.zeros(T, dtype=np.int32)
     for t in range(T):
-        qframes = np.unique(token_frame[t * TILE:min(t * TILE + TILE, tokens)])
-        kframes = np.nonzero(allowed[qframes].any(axis=0))[0]
-        key_ok = np.isin(token_frame, kframes)
+        qf = token_frame[t * TILE:min(t * TILE + TILE, tokens)]
+        if (qf < 0).any():                       # a prefix query sees every key
+            key_ok = np.ones(tokens, dtype=bool)
+        else:
+            kframes = np.nonzero(allowed[np.unique(qf)].any(axis=0))[0]
+            key_ok = (token_frame < 0) | np.isin(token_frame, kframes)
         tiles = np.unique(np.nonzero(key_ok)[0] // TILE)
         idx[t, :len(tiles)] = tiles
         count[t] = len(tiles)
@@ -235,21 +251,43 @@ def window_tiles(tokens: int, frame_tokens: int, chunk_frames: int = 5, neighbou
 
 
 def window_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, frame_tokens: int,
-                     chunk_frames: int = 5, neighbours: int = 1, rows=None) -> np.ndarray:
+                     chunk_frames: int = 5, neighbours: int = 1, rows=None,
+                     prefix: int = 0) -> np.ndarray:
     """Softmax attention restricted to the window and anchor frames, per head.
+
+    The sequence is ``prefix`` non-video tokens (text, audio) followed by the
+    video tokens.  Text and audio interactions stay fully softmax (FreeVideo
+    page, "Where Video DeltaNet comes in"): a prefix query attends to every
+    key, and every query attends to every prefix key; a video query attends to
+    the video keys of its window and of the anchor frames.
 
     q, k, v: [H, N, d] float64.  ``rows`` as in ``dense``.
     """
     H, N, d = q.shape
     rows = np.arange(N) if rows is None else np.asarray(rows)
-    frames = -(-N // frame_tokens)
+    frames, token_frame = _window_token_frames(N, frame_tokens, prefix)
     allowed = window_frames_allowed(frames, chunk_frames, neighbours)
-    token_frame = np.arange(N) // frame_tokens
     out = np.empty((H, len(rows), d), dtype=np.float64)
     qframe = token_frame[rows]
     for h in range(H):
         for f in np.unique(qframe):
             sel = np.nonzero(qframe == f)[0]
-            keys = np.nonzero(allowed[f, token_frame])[0]
+            if f < 0:
+                keys = np.arange(N)
+            else:
+                keys = np.nonzero((token_frame < 0) | allowed[f, np.maximum(token_frame, 0)])[0]
             out[h, sel] = attention_rows(q[h, rows[sel]], k[h, keys], v[h, keys], scale)
     return out
+
+
+def window_density(prefix: int, frames: int, frame_tokens: int, chunk_frames: int = 5,
+                   neighbours: int = 1) -> float:
+    """Fraction of (query, key) pairs the window attends to, prefix included:
+    prefix rows see all N keys, video rows see the P prefix keys plus their
+    allowed video frames (whole frames of frame_tokens tokens)."""
+    allowed = window_frames_allowed(frames, chunk_frames, neighbours).astype(np.float64)
+    video = frames * frame_tokens
+    n = prefix + video
+    pairs = prefix * n + video * prefix + frame_tokens * frame_tokens * allowed.sum()
+    return pairs / (n * n)
+

@@ -173,3 +173,118 @@ def _attention_ignores_window(q, k, v, scale, ft, chunk=5, nb=1, rows=None):
 def test_attention_mutant_caught():
     with pytest.raises(AssertionError):
         check_window_attention(_attention_ignores_window)
+
+
+# ---------------------------------------------------------------- non-video prefix
+# Text and audio tokens stay fully softmax (FreeVideo page, "Where Video
+# DeltaNet comes in"): with P non-video tokens ahead of the video, a prefix
+# query sees every key and every query sees every prefix key.
+
+def brute_token_allowed(N, P, ft, chunk, nb):
+    """Pure-Python restatement at token level: allowed[i][j]."""
+    F = -(-(N - P) // ft)
+    fa = brute_allowed(F, chunk, nb)
+    out = []
+    for i in range(N):
+        row = []
+        for j in range(N):
+            if i < P or j < P:
+                row.append(True)
+            else:
+                row.append(bool(fa[(i - P) // ft][(j - P) // ft]))
+        out.append(row)
+    return out
+
+
+def check_prefix_tiles(fn):
+    for N, P, ft, chunk, nb in [(1000, 37, 64, 2, 1), (900, 300, 100, 3, 1), (1300, 128, 130, 2, 0),
+                                (700, 1, 64, 1, 0), (640, 200, 64, 2, 0)]:
+        allowed = brute_token_allowed(N, P, ft, chunk, nb)
+        idx, count = fn(N, ft, chunk, nb, P)
+        T = -(-N // 128)
+        for t in range(T):
+            want = sorted({j // 128 for i in range(t * 128, min(t * 128 + 128, N))
+                           for j in range(N) if allowed[i][j]})
+            assert count[t] == len(want), (N, P, t)
+            assert list(idx[t, :count[t]]) == want
+            assert np.all(idx[t, count[t]:] == -1)
+
+
+def check_prefix_attention(fn):
+    H, N, d, P, ft = 2, 520, 16, 72, 64
+    q, k, v = (bf16_array((H, N, d), 190 + t) for t in range(3))
+    scale = 0.25
+    allowed = brute_token_allowed(N, P, ft, 2, 0)
+    out = fn(q, k, v, scale, ft, 2, 0, prefix=P)
+    for i in [0, 5, 71, 72, 73, 135, 136, 200, 333, 455, 456, 519]:
+        keys = [j for j in range(N) if allowed[i][j]]
+        for h in range(H):
+            s = [scale * float(q[h, i] @ k[h, j]) for j in keys]
+            m = max(s)
+            p = [math.exp(x - m) for x in s]
+            want = sum(pj * v[h, j] for pj, j in zip(p, keys)) / sum(p)
+            np.testing.assert_allclose(out[h, i], want, rtol=0, atol=1e-12)
+    # prefix rows are dense rows, bit for bit
+    dense = oracle.dense(q, k, v, scale, rows=np.arange(P))
+    assert np.array_equal(out[:, :P], dense)
+    # Q = 0: the mean of V over the allowed keys
+    z = fn(np.zeros_like(q), k, v, scale, ft, 2, 0, prefix=P)
+    for i in [3, 100, 300, 519]:
+        keys = [j for j in range(N) if allowed[i][j]]
+        np.testing.assert_allclose(z[:, i], v[:, keys].mean(axis=1), atol=1e-13)
+
+
+def test_prefix_window_tiles_brute_force():
+    check_prefix_tiles(oracle.window_tiles)
+
+
+def test_prefix_window_attention_brute_force():
+    check_prefix_attention(oracle.window_attention)
+
+
+def test_prefix_zero_is_the_video_only_window():
+    H, N, d = 1, 700, 16
+    q, k, v = (bf16_array((H, N, d), 290 + t) for t in range(3))
+    a = oracle.window_attention(q, k, v, 0.25, 64, 2, 1)
+    b = oracle.window_attention(q, k, v, 0.25, 64, 2, 1, prefix=0)
+    assert np.array_equal(a, b)
+
+
+def test_window_density_counts_the_prefix():
+    # brute-force count of the token-level mask against the closed form
+    for P, F, ft, chunk, nb in [(0, 7, 3, 2, 1), (5, 7, 3, 2, 1), (11, 9, 4, 3, 0), (2, 12, 5, 5, 1)]:
+        N = P + F * ft
+        a = brute_token_allowed(N, P, ft, chunk, nb)
+        want = sum(sum(r) for r in a) / (N * N)
+        assert abs(oracle.window_density(P, F, ft, chunk, nb) - want) < 1e-15
+    # prefix 0 reduces to the frame-level density pinned above
+    assert abs(oracle.window_density(0, 42, 1008) - 0.40023) < 1e-4
+
+
+def _prefix_hidden(q, k, v, scale, ft, chunk=5, nb=1, rows=None, prefix=0):
+    # video rows lose the prefix keys
+    H, N, d = q.shape
+    out = oracle.window_attention(q, k, v, scale, ft, chunk, nb, rows=rows, prefix=prefix)
+    vid = oracle.window_attention(q[:, prefix:], k[:, prefix:], v[:, prefix:], scale, ft, chunk, nb)
+    out[:, prefix:] = vid
+    return out
+
+
+def _prefix_as_frames(q, k, v, scale, ft, chunk=5, nb=1, rows=None, prefix=0):
+    # frames counted from token 0 instead of from the first video token
+    return oracle.window_attention(q, k, v, scale, ft, chunk, nb, rows=rows, prefix=0)
+
+
+@pytest.mark.parametrize("mut", [_prefix_hidden, _prefix_as_frames], ids=lambda f: f.__name__)
+def test_prefix_attention_mutants_caught(mut):
+    with pytest.raises(AssertionError):
+        check_prefix_attention(mut)
+
+
+def _prefix_tiles_ignored(N, ft, chunk=5, nb=1, prefix=0):
+    return A.window_tiles(N, ft, chunk, nb, 0)
+
+
+def test_prefix_tiles_mutant_caught():
+    with pytest.raises(AssertionError):
+        check_prefix_tiles(_prefix_tiles_ignored)
