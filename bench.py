@@ -57,16 +57,20 @@ def sparse_flops(idx, tokens: int, d: int = 128) -> float:
     return float(4 * d * (keys * valid[None, :]).sum())
 
 
-def window_flops(tokens: int, frame_tokens: int, chunk: int, nb: int, heads: int, d: int = 128) -> float:
-    """QK^T + PV FLOPs over the (query, key) pairs the frame window allows."""
+def window_flops(tokens: int, frame_tokens: int, chunk: int, nb: int, heads: int, d: int = 128,
+                 prefix: int = 0) -> float:
+    """QK^T + PV FLOPs over the (query, key) pairs the frame window allows;
+    `prefix` non-video tokens ahead of the video see and are seen by all."""
     import numpy as np
-    frames = -(-tokens // frame_tokens)
+    video = tokens - prefix
+    frames = -(-video // frame_tokens)
     f = np.arange(frames)
     allowed = np.abs(f[:, None] // chunk - f[None, :] // chunk) <= nb
     allowed[:, [0, frames - 1]] = True
     allowed[[0, frames - 1], :] = True
-    per_frame = np.minimum(frame_tokens, tokens - f * frame_tokens).astype(np.float64)
+    per_frame = np.minimum(frame_tokens, video - f * frame_tokens).astype(np.float64)
     pairs = float(per_frame @ allowed.astype(np.float64) @ per_frame)
+    pairs += float(prefix) * tokens + float(video) * prefix
     return 4.0 * d * heads * pairs
 
 
@@ -134,7 +138,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8", "vda", "roofline"],
+    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8", "vda", "roofline",
+                                       "configs"],
                     default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
                          "0 for window, vsa, int8, vda and roofline, which are timed outside the step)")
@@ -189,6 +194,7 @@ def main():
     do_vsa = args.only in (None, "vsa")
     do_int8 = args.only in (None, "int8")
     do_vda = args.only in (None, "vda")
+    do_configs = args.only in (None, "configs")
     do_roofline = args.only in (None, "dense", "roofline")
     if not do_dense:
         flop_dense = 0.0
@@ -329,6 +335,60 @@ def main():
             int8["rel_diff_vs_bf16_dense"] = round(float(d.norm() / out_dense.float().norm()), 5)
         del out_i8
 
+    # the other workloads of the path, outside the step, each on its own seeded
+    # inputs: 5,040 tokens x 56 heads dense in one launch; 72,576 x 16 heads
+    # dense (one 16-head group); 102,816 tokens x 56 heads (14.4 s clip, last
+    # tile 32 tokens) dense and 90% sparse in 8-head groups
+    configs = None
+    if do_configs:
+        configs = {}
+
+        def timed(fn, reps=3):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                ev[0].record(stream)
+                fn()
+                ev[1].record(stream)
+                torch.cuda.synchronize()
+                ts.append(ev[0].elapsed_time(ev[1]))
+            return float(np.median(ts))
+
+        def entry(ms, flop):
+            tf = flop / (ms * 1e-3) / 1e12
+            return {"ms": round(ms, 3), "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "flop": flop}
+
+        for cid in (2, 3, 5):
+            c = inputs.CONFIGS[cid]
+            log("generating", c.name)
+            cq, ck, cv = (t.to(dev) for t in inputs.make_inputs(cid))
+            cout = torch.empty_like(cq)
+            fd = 4.0 * c.tokens * c.tokens * 128 * c.heads
+            if c.group == c.heads:
+                dms = timed(lambda: fv.forward(cq, ck, cv, scale=c.scale, out=cout))
+            else:
+                dms = timed(lambda: fv.forward_heads(cq, ck, cv, c.group, scale=c.scale, out=cout))
+            rec = {"workload": f"{c.tokens:,} tokens x {c.heads} heads, "
+                               + (f"one launch" if c.group == c.heads else f"{c.group}-head groups"),
+                   "dense": entry(dms, fd)}
+            if "sparse" in c.modes:
+                cidx = fv.select_tiles(cq, ck, keep_frac=c.keep_frac)
+                torch.cuda.synchronize()
+                fs = sparse_flops(cidx.cpu().numpy(), c.tokens)
+                keep = int(cidx.shape[2])
+                del cidx
+                sms = timed(lambda: fv.forward_heads(cq, ck, cv, c.group, scale=c.scale, mode="sparse",
+                                                     keep_frac=c.keep_frac, out=cout))
+                rec["sparse"] = entry(sms, fs)
+                rec["sparse"]["keep_tiles"] = keep
+                rec["sparse"]["speedup_vs_dense"] = round(dms / sms, 3)
+            configs[c.name] = rec
+            del cq, ck, cv, cout
+            torch.cuda.empty_cache()
+
     # VSA-H3 packed sequence, outside the step: a 512-token non-video prefix
     # ahead of the same 72 x 24 x 42 video grid, (4, 4, 4) tiles, 90% sparse,
     # all 56 heads in one call (new inputs: the prefix shifts the video tokens)
@@ -350,6 +410,27 @@ def main():
             if i:
                 v_ms.append(v_ev[0].elapsed_time(v_ev[1]))
         vidx = fv.vsa_select(pq, pk, prefix, grid, tile, KEEP_FRAC).cpu().numpy()
+        # the frame window on the same packed sequence: the 512 non-video
+        # tokens are dense rows and columns (text and audio stay fully softmax)
+        window_prefix = None
+        if do_window:
+            ft = grid[1] * grid[2]
+            for i in range(4):
+                v_ev[0].record(stream)
+                fv.forward_window(pq, pk, pv, frame_tokens=ft, chunk_frames=5, neighbours=1, scale=scale,
+                                  prefix=prefix, out=pout)
+                v_ev[1].record(stream)
+                torch.cuda.synchronize()
+                if i == 0:
+                    wp_ms = []
+                else:
+                    wp_ms.append(v_ev[0].elapsed_time(v_ev[1]))
+            ntok = prefix + grid[0] * ft
+            flop_wp = window_flops(ntok, ft, 5, 1, HEADS, prefix=prefix)
+            wpm = float(np.median(wp_ms))
+            window_prefix = {"ms": round(wpm, 3), "prefix": prefix, "tokens": ntok, "flop_allowed": flop_wp,
+                             "tflops_effective": round(flop_wp / (wpm * 1e-3) / 1e12, 2),
+                             "density": round(flop_wp / (4.0 * ntok * ntok * 128 * HEADS), 4)}
         del pq, pk, pv, pout
         vm = float(np.median(v_ms))
         flop_v = vsa_flops(vidx, prefix, grid, tile)
@@ -450,10 +531,14 @@ def main():
         if do_dense:
             window["speedup_vs_dense"] = round(d_ms / window["ms"], 3)
         result["window"] = window
+        if do_vsa and window_prefix is not None:
+            result["window"]["with_prefix"] = window_prefix
     if vsa is not None:
         result["vsa"] = vsa
     if vda is not None:
         result["vda"] = vda
+    if configs is not None:
+        result["configs"] = configs
     if int8 is not None:
         if do_dense:
             int8["speedup_vs_dense"] = round(d_ms / int8["ms"], 3)

@@ -175,26 +175,35 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
                          double keep_frac, void* stream);
 
 /* Frame-window softmax, the softmax branch of Video DeltaNet (FreeVideo page,
- * section "Where Video DeltaNet comes in"): exact softmax attention in which
- * a query of latent frame qf sees a key of latent frame kf only if
+ * section "Where Video DeltaNet comes in"): exact softmax attention over a
+ * packed sequence of prefix_tokens non-video tokens (text, audio) followed by
+ * the video tokens.  Text and audio interactions stay fully softmax: a
+ * non-video query sees every key and every query sees every non-video key.
+ * A video query of latent frame qf sees a video key of latent frame kf only if
  * |qf / chunk_frames - kf / chunk_frames| <= neighbours (integer division;
  * chunks counted from frame 0) or kf or qf is the first or the last frame.
- * Latent frame of token i = i / frame_tokens (1,008 at 1344x768; chunks of 5
- * frames with 1 neighbour on each side give the page's 15-frame window).
- * q, k, v, out as in fvattn_forward.  frame_tokens >= 64 (else
- * FVATTN_ERR_UNSUPPORTED), chunk_frames >= 1, neighbours >= 0.  Uses
- * stream-ordered scratch for the key-tile lists (ceil(tokens/128) * (T + 1)
- * int32). */
+ * Latent frame of video token i = (i - prefix_tokens) / frame_tokens (1,008
+ * at 1344x768; chunks of 5 frames with 1 neighbour on each side give the
+ * page's 15-frame window); the last frame may be partial.  A sequence whose
+ * non-video tokens sit elsewhere (say audio after the video) is a permutation
+ * of this layout: the attention is permutation-equivariant, so the caller
+ * packs it as [non-video | video].
+ * q, k, v, out as in fvattn_forward.  0 <= prefix_tokens <= tokens (else
+ * FVATTN_ERR_INVALID_ARG), frame_tokens >= 64 (else FVATTN_ERR_UNSUPPORTED),
+ * chunk_frames >= 1, neighbours >= 0.  Uses stream-ordered scratch for the
+ * key-tile lists (ceil(tokens/128) * (T + 1) int32). */
 int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
-                          int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,
-                          int neighbours, void* stream);
+                          int tokens, int head_dim, float scale, int prefix_tokens,
+                          int frame_tokens, int chunk_frames, int neighbours, void* stream);
 
 /* The key-tile lists fvattn_forward_window walks: for each 128-token query
  * tile t, the ascending indices of the key tiles holding at least one key that
- * some query of t may attend to.  idx_out: int32 [T][T] device, row t holds
- * count_out[t] indices followed by -1; count_out: int32 [T] device. */
-int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neighbours,
-                        int32_t* idx_out, int32_t* count_out, void* stream);
+ * some query of t may attend to (a tile holding a non-video query lists every
+ * tile; a tile holding a non-video key is listed for every query tile).
+ * idx_out: int32 [T][T] device, row t holds count_out[t] indices followed by
+ * -1; count_out: int32 [T] device. */
+int fvattn_window_tiles(int tokens, int prefix_tokens, int frame_tokens, int chunk_frames,
+                        int neighbours, int32_t* idx_out, int32_t* count_out, void* stream);
 
 /* VSA-H3 packed-sequence attention (FastH3 page, section "Lever two: VSA-H3
  * makes each of the four calls cheaper").  The sequence is packed as

@@ -183,8 +183,8 @@ def test_binding_rejects_cpu_tensors():
 
 
 def _win(lib, q=BOGUS, k=BOGUS, v=BOGUS, o=BOGUS, heads=4, tokens=1008 * 12, hd=128, scale=0.088,
-         ft=1008, chunk=5, nb=1):
-    return lib.fvattn_forward_window(q, k, v, o, heads, tokens, hd, scale, ft, chunk, nb, NULL)
+         ft=1008, chunk=5, nb=1, prefix=0):
+    return lib.fvattn_forward_window(q, k, v, o, heads, tokens, hd, scale, prefix, ft, chunk, nb, NULL)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -200,6 +200,8 @@ def _win(lib, q=BOGUS, k=BOGUS, v=BOGUS, o=BOGUS, heads=4, tokens=1008 * 12, hd=
     (dict(ft=63), fv.FVATTN_ERR_UNSUPPORTED),
     (dict(ft=0), fv.FVATTN_ERR_UNSUPPORTED),
     (dict(tokens=2049 * 128), fv.FVATTN_ERR_UNSUPPORTED),
+    (dict(prefix=-1), fv.FVATTN_ERR_INVALID_ARG),
+    (dict(prefix=1008 * 12 + 1), fv.FVATTN_ERR_INVALID_ARG),
 ])
 def test_forward_window_rejects_bad_arguments(lib, kw, want):
     assert _win(lib, **kw) == want
@@ -209,14 +211,16 @@ def test_window_entry_points_empty_and_bad(lib):
     assert _win(lib, q=NULL, k=NULL, v=NULL, o=NULL, heads=0) == fv.FVATTN_OK
     assert _win(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0) == fv.FVATTN_OK
     wt = lib.fvattn_window_tiles
-    assert wt(0, 1008, 5, 1, NULL, NULL, NULL) == fv.FVATTN_OK
-    assert wt(-1, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
-    assert wt(5000, 1008, 0, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
-    assert wt(5000, 1008, 5, -1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
-    assert wt(5000, 32, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
-    assert wt(5000, 1008, 5, 1, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
-    assert wt(5000, 1008, 5, 1, BOGUS, NULL, NULL) == fv.FVATTN_ERR_INVALID_ARG
-    assert wt(2049 * 128, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert wt(0, 0, 1008, 5, 1, NULL, NULL, NULL) == fv.FVATTN_OK
+    assert wt(-1, 0, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 0, 1008, 0, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 0, 1008, 5, -1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, -1, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 5001, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 0, 32, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
+    assert wt(5000, 0, 1008, 5, 1, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(5000, 0, 1008, 5, 1, BOGUS, NULL, NULL) == fv.FVATTN_ERR_INVALID_ARG
+    assert wt(2049 * 128, 0, 1008, 5, 1, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
 
 
 def test_window_alloc_failure_hook(lib, monkeypatch):

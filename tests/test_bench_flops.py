@@ -45,6 +45,21 @@ def test_window_flops_counts_the_allowed_pairs(N, ft, chunk, nb):
     assert bench.window_flops(N, ft, chunk, nb, heads=3) == 4.0 * D * 3 * pairs
 
 
+@pytest.mark.parametrize("N,P,ft,chunk,nb", [(1000, 37, 64, 2, 1), (700, 300, 100, 3, 0), (5040, 128, 1008, 5, 1),
+                                             (128, 64, 64, 5, 1)])
+def test_window_flops_with_prefix_counts_the_allowed_pairs(N, P, ft, chunk, nb):
+    frames = -(-(N - P) // ft)
+    allowed = oracle.window_frames_allowed(frames, chunk, nb)
+    f = np.arange(N - P) // ft
+    pairs = int(allowed[f][:, f].sum()) + P * N + (N - P) * P
+    assert bench.window_flops(N, ft, chunk, nb, heads=3, prefix=P) == 4.0 * D * 3 * pairs
+    # the oracle's own output agrees on which keys a row sees: a window over a
+    # whole-frame video part has the oracle's closed-form density
+    if (N - P) % ft == 0:
+        dens = oracle.window_density(P, frames, ft, chunk, nb)
+        assert abs(bench.window_flops(N, ft, chunk, nb, heads=1, prefix=P) / (4.0 * D * N * N) - dens) < 1e-12
+
+
 @pytest.mark.parametrize("prefix,grid,tile,keep", [(37, (5, 6, 7), (4, 4, 4), 3), (0, (4, 8, 8), (4, 8, 8), 1),
                                                   (100, (9, 10, 6), (4, 4, 4), 5)])
 def test_vsa_flops_counts_prefix_rows_and_kept_tiles(prefix, grid, tile, keep):

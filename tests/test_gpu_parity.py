@@ -330,6 +330,48 @@ def test_window_covering_everything_is_dense_bitwise(N, ft):
     assert torch.equal(a, b)
 
 
+# Non-video prefix (text, audio): dense rows and columns ahead of the video.
+
+WINDOW_PREFIX_CASES = [
+    # prefix, (frames, height, width) of the video grid (frame_tokens = h w), chunk, neighbours
+    (1, (3, 8, 8), 1, 0), (37, (11, 8, 8), 2, 1), (64, (9, 8, 8), 2, 0), (127, (10, 8, 8), 2, 1),
+    (128, (10, 8, 8), 2, 0), (129, (7, 10, 10), 3, 1), (300, (9, 10, 10), 3, 1),
+    (512, (5, 24, 42), 5, 1), (700, (2, 8, 8), 1, 0),
+]
+
+
+@pytest.mark.parametrize("prefix,grid,chunk,nb", WINDOW_PREFIX_CASES + [
+    (512, (72, 24, 42), 5, 1), (512, (102, 24, 42), 5, 1), (3000, (42, 24, 42), 5, 1)])
+def test_window_tiles_with_prefix_bit_exact(prefix, grid, chunk, nb):
+    N, ft = prefix + grid[0] * grid[1] * grid[2], grid[1] * grid[2]
+    say("window tiles with prefix", prefix, grid, chunk, nb)
+    idx, count = fv.window_tiles(N, ft, chunk, nb, prefix=prefix, device=DEV)
+    ref_idx, ref_count = oracle.window_tiles(N, ft, chunk, nb, prefix)
+    assert np.array_equal(count.cpu().numpy(), ref_count)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+@pytest.mark.parametrize("prefix,grid,chunk,nb", WINDOW_PREFIX_CASES)
+def test_window_attention_with_prefix_matches_oracle(prefix, grid, chunk, nb):
+    say("window attention with prefix", prefix, grid, chunk, nb)
+    q, k, v = inputs.make_packed_qkv(prefix, grid, 2, 400 + prefix)
+    ft = grid[1] * grid[2]
+    out = fv.forward_window(*to_dev(q, k, v), frame_tokens=ft, chunk_frames=chunk, neighbours=nb,
+                            prefix=prefix).cpu()
+    ref = oracle.window_attention(*(oracle.widen(t) for t in (q, k, v)), 1 / math.sqrt(128), ft, chunk,
+                                  nb, prefix=prefix)
+    assert_close(oracle.widen(out), ref, f"window prefix={prefix} grid={grid} chunk={chunk} nb={nb}")
+
+
+@pytest.mark.parametrize("N", [1000, 129, 64])
+def test_window_all_prefix_is_dense_bitwise(N):
+    # every token non-video: every query sees every key, in dense order
+    q, k, v = to_dev(*inputs.make_qkv(N, 3, "iid", 90 + N))
+    a = fv.forward_window(q, k, v, frame_tokens=64, chunk_frames=1, neighbours=0, prefix=N)
+    b = fv.forward(q, k, v, mode="dense")
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------------ VSA-H3 packed sequence
 
 VSA_CASES = [
@@ -607,6 +649,27 @@ def test_config4_window(cfg4):
 @pytest.mark.timeout(300)
 def test_config5_window(cfg5):
     _full_size_window(5, cfg5)
+
+
+@pytest.mark.timeout(600)
+def test_window_with_prefix_full_size():
+    # 512 non-video tokens + 72 latent frames of 24 x 42 (a 10 s clip), 8 heads:
+    # every row of head 0, sampled rows of every head
+    prefix, grid = inputs.VSA_PREFIX, inputs.VSA_GRID_72
+    q, k, v = inputs.make_packed_qkv(prefix, grid, 8, 13)
+    N, ft = q.shape[1], grid[1] * grid[2]
+    out = fv.forward_window(*to_dev(q, k, v), frame_tokens=ft, chunk_frames=5, neighbours=1,
+                            prefix=prefix).cpu()
+    rows = sorted(set([0, 1, prefix - 1, prefix, prefix + 1, prefix + 1007, prefix + 1008,
+                       prefix + 5 * 1008, N - 1009, N - 2, N - 1]
+                      + np.random.default_rng(14).integers(0, N, 24).tolist()))
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    ref = oracle.window_attention(qw, kw, vw, 1 / math.sqrt(128), ft, 5, 1, rows=rows, prefix=prefix)
+    assert_close(oracle.widen(out[:, rows]), ref, "window prefix 512 + 72,576 sampled rows, 8 heads")
+    q0, k0, v0 = qw[:1], kw[:1], vw[:1]
+    ref0 = _oracle_rows(lambda r: oracle.window_attention(q0, k0, v0, 1 / math.sqrt(128), ft, 5, 1,
+                                                          rows=r, prefix=prefix), N)
+    assert_close(oracle.widen(out[:1]), ref0, f"window prefix 512 + 72,576 head 0 all {N} rows")
 
 
 @pytest.fixture(scope="module")

@@ -47,8 +47,8 @@ SIGNATURES = {
     "fvattn_forward_sparse_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _D, _P]),
     "fvattn_forward_heads": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _D, _P]),
     "fvattn_tile_means": (_I, [_P, _I, _I, _I, _P, _P]),
-    "fvattn_forward_window": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _P]),
-    "fvattn_window_tiles": (_I, [_I, _I, _I, _I, _P, _P, _P]),
+    "fvattn_forward_window": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
+    "fvattn_window_tiles": (_I, [_I, _I, _I, _I, _I, _P, _P, _P]),
     "fvattn_tile_scores": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "fvattn_forward_vsa": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _I, _I, _I, _I, _I, _I, _D, _P]),
     "fvattn_vsa_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _P, _P]),
@@ -242,8 +242,9 @@ def tile_scores(qm, km, stream=None):
 
 
 def forward_window(q, k, v, frame_tokens: int = 1008, chunk_frames: int = 5, neighbours: int = 1,
-                   scale: float | None = None, out=None, stream=None):
-    """fvattn_forward_window: softmax restricted to the frame window and the anchor frames."""
+                   scale: float | None = None, prefix: int = 0, out=None, stream=None):
+    """fvattn_forward_window: softmax restricted to the frame window and the anchor
+    frames; `prefix` non-video tokens (text, audio) ahead of the video stay dense."""
     torch = _torch()
     H, N, d = _check_qkv(q, k, v)
     if out is None:
@@ -252,20 +253,20 @@ def forward_window(q, k, v, frame_tokens: int = 1008, chunk_frames: int = 5, nei
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):
         _check(load().fvattn_forward_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), H, N, d, scale,
-                                            int(frame_tokens), int(chunk_frames), int(neighbours),
-                                            _stream_ptr(stream)))
+                                            int(prefix), int(frame_tokens), int(chunk_frames),
+                                            int(neighbours), _stream_ptr(stream)))
     return out
 
 
 def window_tiles(tokens: int, frame_tokens: int = 1008, chunk_frames: int = 5, neighbours: int = 1,
-                 device="cuda", stream=None):
+                 prefix: int = 0, device="cuda", stream=None):
     """fvattn_window_tiles: (idx int32 [T, T] padded with -1, count int32 [T]) on the device."""
     torch = _torch()
     T = tile_count(tokens)
     idx = torch.empty((T, T), dtype=torch.int32, device=device)
     count = torch.empty((T,), dtype=torch.int32, device=device)
     with torch.cuda.device(idx.device):
-        _check(load().fvattn_window_tiles(int(tokens), int(frame_tokens), int(chunk_frames),
+        _check(load().fvattn_window_tiles(int(tokens), int(prefix), int(frame_tokens), int(chunk_frames),
                                           int(neighbours), _ptr(idx), _ptr(count), _stream_ptr(stream)))
     return idx, count
 

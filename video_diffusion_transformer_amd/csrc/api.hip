@@ -403,9 +403,16 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
   return FVATTN_OK;
 }
 
-int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neighbours,
-                        int32_t* idx_out, int32_t* count_out, void* stream) {
-  if (tokens < 0 || chunk_frames < 1 || neighbours < 0) return FVATTN_ERR_INVALID_ARG;
+// Video frames after a prefix of `prefix` tokens (the last may be partial).
+int window_frames(int tokens, int prefix, int frame_tokens) {
+  return tokens > prefix ? (tokens - prefix - 1) / frame_tokens + 1 : 0;
+}
+
+int fvattn_window_tiles(int tokens, int prefix_tokens, int frame_tokens, int chunk_frames,
+                        int neighbours, int32_t* idx_out, int32_t* count_out, void* stream) {
+  if (tokens < 0 || chunk_frames < 1 || neighbours < 0 || prefix_tokens < 0 ||
+      prefix_tokens > tokens)
+    return FVATTN_ERR_INVALID_ARG;
   if (frame_tokens < 64) return FVATTN_ERR_UNSUPPORTED;
   if (tokens == 0) return FVATTN_OK;
   if (!idx_out || !count_out) return FVATTN_ERR_INVALID_ARG;
@@ -413,18 +420,20 @@ int fvattn_window_tiles(int tokens, int frame_tokens, int chunk_frames, int neig
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
   fvattn::ListParams wp;
+  wp.prefix = prefix_tokens;
   wp.frame_tokens = frame_tokens;
   wp.chunk_frames = chunk_frames;
   wp.neighbours = neighbours;
-  wp.frames = (tokens - 1) / frame_tokens + 1;
+  wp.frames = window_frames(tokens, prefix_tokens, frame_tokens);
   return hip_status(
       fvattn::launch_window_tiles(tokens, wp, kTile, false, idx_out, count_out, (hipStream_t)stream));
 }
 
 int fvattn_forward_window(const void* q, const void* k, const void* v, void* out, int heads,
-                          int tokens, int head_dim, float scale, int frame_tokens, int chunk_frames,
-                          int neighbours, void* stream) {
-  if (heads < 0 || tokens < 0 || !scale_ok(scale) || chunk_frames < 1 || neighbours < 0)
+                          int tokens, int head_dim, float scale, int prefix_tokens,
+                          int frame_tokens, int chunk_frames, int neighbours, void* stream) {
+  if (heads < 0 || tokens < 0 || !scale_ok(scale) || chunk_frames < 1 || neighbours < 0 ||
+      prefix_tokens < 0 || prefix_tokens > tokens)
     return FVATTN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || frame_tokens < 64) return FVATTN_ERR_UNSUPPORTED;
   if (heads == 0 || tokens == 0) return FVATTN_OK;
@@ -445,11 +454,17 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   int32_t* counts = (int32_t*)((char*)scratch + idx_bytes);
   fvattn::ListParams wp;
   wp.counts = counts;
+  wp.prefix = prefix_tokens;
   wp.frame_tokens = frame_tokens;
   wp.chunk_frames = chunk_frames;
   wp.neighbours = neighbours;
-  wp.frames = (tokens - 1) / frame_tokens + 1;
-  wp.first_block = (int)((long long)(wp.frames - 1) * frame_tokens / fvattn::kWindowRows);
+  wp.frames = window_frames(tokens, prefix_tokens, frame_tokens);
+  // the blocks of the last frame (rows that see every key) are walked first
+  wp.first_block =
+      wp.frames > 0
+          ? (int)(((long long)prefix_tokens + (long long)(wp.frames - 1) * frame_tokens) /
+                  fvattn::kWindowRows)
+          : 0;
   // the layout allocated above: launch_window_tiles writes `blocks` lists of
   // kWindowRows rows, T entries apart; the attention launcher checks it again
   wp.list_rows = fvattn::kWindowRows;

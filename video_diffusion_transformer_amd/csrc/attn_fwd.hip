@@ -438,22 +438,27 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   // Frame 0 is an anchor and every list starts with key tile 0, so stage 0
   // (keys 0..63, all of frame 0) is open to every row: the running max is
   // finite from the prologue on, and a later stage masked whole for a row adds
-  // exp2(-inf) = 0 to it.
+  // exp2(-inf) = 0 to it.  Non-video tokens (text, audio) ahead of the video:
+  // frames are counted from the first video token, a prefix query is treated
+  // as an anchor (it sees every key), and a stage holding prefix keys can
+  // only hold frame-0 keys besides them (frame_tokens >= 64), all open to
+  // every query: the prefix keys fall in the stage's first frame (ok0).
   int q_chunk[kQB];
   bool q_anchor[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    const int qf = kMode == 2 ? (q0 + 32 * qb + l32) / wp.frame_tokens : 0;
+    const int qrow = q0 + 32 * qb + l32;
+    const int qf = kMode == 2 && qrow >= wp.prefix ? (qrow - wp.prefix) / wp.frame_tokens : 0;
     q_chunk[qb] = kMode == 2 ? qf / wp.chunk_frames : 0;
-    q_anchor[qb] = qf == 0 || qf >= wp.frames - 1;
+    q_anchor[qb] = qrow < wp.prefix || qf == 0 || qf >= wp.frames - 1;
   }
   auto frame_ok = [&](int qb, int kf) {
     const int dc = q_chunk[qb] - kf / wp.chunk_frames;
     return q_anchor[qb] || kf == 0 || kf == wp.frames - 1 || (dc <= wp.neighbours && -dc <= wp.neighbours);
   };
   auto window_mask = [&](f32x16 (&S)[kQB][kKB], int kv0) {
-    const int kf0 = kv0 / wp.frame_tokens;
-    const int next_frame = (kf0 + 1) * wp.frame_tokens;   // first key of frame kf0 + 1
+    const int kf0 = (kv0 > wp.prefix ? kv0 - wp.prefix : 0) / wp.frame_tokens;
+    const int next_frame = wp.prefix + (kf0 + 1) * wp.frame_tokens;   // first key of frame kf0 + 1
     bool ok0[kQB], ok1[kQB];
     bool need = kv0 + kBN > N;
 #pragma unroll

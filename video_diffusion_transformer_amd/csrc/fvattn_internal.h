@@ -75,12 +75,16 @@ constexpr int kVsaCountShift = 16, kVsaGroupShift = 22;
 // 64 (one group per 64 rows, at most four groups), one wave per 32 rows.
 constexpr int kVsaRows = 128;
 
-// Per-launch parameters of the list-driven modes.  Frame window: latent
-// frames of frame_tokens tokens, chunks of chunk_frames frames, `neighbours`
-// chunks on each side, first and last frame as anchors; counts[b] = number of
-// list entries of query block b.  VSA: the geometry above, and counts[h B + b].
+// Per-launch parameters of the list-driven modes.  Frame window: `prefix`
+// non-video tokens, then latent frames of frame_tokens tokens, chunks of
+// chunk_frames frames, `neighbours` chunks on each side, first and last frame
+// as anchors; counts[b] = number of list entries of query block b.  VSA: the
+// geometry above, and counts[h B + b].
 struct ListParams {
   const int32_t* counts = nullptr;
+  // Frame window: non-video tokens (text, audio) ahead of the video; they see
+  // and are seen by every token, and video frames are counted after them
+  int prefix = 0;
   int frame_tokens = 0;
   int chunk_frames = 1;
   int neighbours = 0;

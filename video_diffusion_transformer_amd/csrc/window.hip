@@ -5,7 +5,9 @@
 //
 // One wave per block of q_rows query tokens (128, the tile size, for both the
 // public lists and the attention workgroups).  A key tile is listed when some query of the
-// block may attend to some key of it.  Frames inside a tile are contiguous
+// block may attend to some key of it.  Non-video tokens (text, audio) ahead of
+// the video stay fully softmax: a block holding a prefix row lists every
+// tile, and a tile holding a prefix key is listed for every block.  Frames inside a tile are contiguous
 // and chunks grow with frames, so this is a closed-form interval test: either
 // tile holds an anchor frame, or the chunk ranges of the two tiles lie within
 // `neighbours` of each other.  Listed tiles are compacted in ascending order
@@ -27,10 +29,13 @@ __global__ __launch_bounds__(64) void window_tiles_kernel(int N, ListParams wp, 
                                                           int32_t* __restrict__ idx,
                                                           int32_t* __restrict__ counts) {
   const int t = blockIdx.x, lane = threadIdx.x;
-  const int ft = wp.frame_tokens, chunk = wp.chunk_frames, nb = wp.neighbours;
+  const int P = wp.prefix, ft = wp.frame_tokens, chunk = wp.chunk_frames, nb = wp.neighbours;
   const int last = wp.frames - 1;
   const int q_lo = t * q_rows, q_hi = (q_lo + q_rows < N ? q_lo + q_rows : N) - 1;
-  const int qf_lo = q_lo / ft, qf_hi = q_hi / ft;
+  // prefix rows see every key; the frame arithmetic below is for the
+  // block's video rows [max(q_lo, P), q_hi] (none when q_hi < P)
+  const bool q_pre = q_lo < P, q_vid = q_hi >= P;
+  const int qf_lo = ((q_lo > P ? q_lo : P) - P) / ft, qf_hi = (q_hi - P) / ft;
   const bool q_anchor = qf_lo == 0 || qf_hi >= last;
   const int qc_lo = qf_lo / chunk, qc_hi = qf_hi / chunk;
   // non-anchor query frames [qa_lo, qa_hi] (empty when qa_lo > qa_hi)
@@ -44,12 +49,15 @@ __global__ __launch_bounds__(64) void window_tiles_kernel(int N, ListParams wp, 
     int entry = j;
     if (j < T) {
       const int k_lo = j * kTile, k_hi = (k_lo + kTile < N ? k_lo + kTile : N) - 1;
-      const int kf_lo = k_lo / ft, kf_hi = k_hi / ft;
+      const bool k_pre = k_lo < P, k_vid = k_hi >= P;
+      const int kf_lo = ((k_lo > P ? k_lo : P) - P) / ft, kf_hi = (k_hi - P) / ft;
       const bool k_anchor = kf_lo == 0 || kf_hi >= last;
       const int kc_lo = kf_lo / chunk, kc_hi = kf_hi / chunk;
-      need = q_anchor || k_anchor || (kc_lo <= qc_hi + nb && kc_hi >= qc_lo - nb);
+      const bool video_need =
+          q_vid && k_vid && (q_anchor || k_anchor || (kc_lo <= qc_hi + nb && kc_hi >= qc_lo - nb));
+      need = q_pre || k_pre || video_need;
       const int ka_lo = kf_lo > 1 ? kf_lo : 1, ka_hi = kf_hi < last - 1 ? kf_hi : last - 1;
-      const bool all_ok = qa_lo > qa_hi || ka_lo > ka_hi ||
+      const bool all_ok = !q_vid || !k_vid || qa_lo > qa_hi || ka_lo > ka_hi ||
                           (ka_hi / chunk - qa_lo / chunk <= nb && qa_hi / chunk - ka_lo / chunk <= nb);
       if (flags && (!all_ok || k_hi - k_lo + 1 < kTile)) entry |= kMaskFlag;
     }
