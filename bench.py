@@ -138,8 +138,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8", "vda", "roofline",
-                                       "configs"],
+    ap.add_argument("--only", choices=["dense", "sparse", "window", "vsa", "int8", "fp8", "vda",
+                                       "roofline", "configs"],
                     default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
                          "0 for window, vsa, int8, vda and roofline, which are timed outside the step)")
@@ -193,6 +193,7 @@ def main():
     do_window = args.only in (None, "window")
     do_vsa = args.only in (None, "vsa")
     do_int8 = args.only in (None, "int8")
+    do_fp8 = args.only in (None, "fp8")
     do_vda = args.only in (None, "vda")
     do_configs = args.only in (None, "configs")
     do_roofline = args.only in (None, "dense", "roofline")
@@ -311,29 +312,34 @@ def main():
                   "tflops_visited": round(flop_w_visited / (wm * 1e-3) / 1e12, 2),
                   "density": round(flop_w / (4.0 * TOKENS * TOKENS * 128 * HEADS), 4)}
 
-    # dense attention with INT8 query-key scores, outside the step: same
-    # inputs, same head groups
-    int8 = None
-    if do_int8:
-        out_i8 = torch.empty_like(qd)
+    # dense attention with INT8 and with FP8 (E4M3) query-key scores, outside
+    # the step: same inputs, same head groups
+    quant = {}
+    for qmode, on in (("int8", do_int8), ("fp8", do_fp8)):
+        if not on:
+            continue
+        out_q = torch.empty_like(qd)
         i_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         i_ms = []
         for i in range(4):
             i_ev[0].record(stream)
-            fv.forward_heads(qd, kd, vd, GROUP, scale=scale, mode="int8", out=out_i8)
+            fv.forward_heads(qd, kd, vd, GROUP, scale=scale, mode=qmode, out=out_q)
             i_ev[1].record(stream)
             torch.cuda.synchronize()
             if i:
                 i_ms.append(i_ev[0].elapsed_time(i_ev[1]))
         im = float(np.median(i_ms))
         flop_i = 4.0 * TOKENS * TOKENS * 128 * HEADS
-        int8 = {"ms": round(im, 3), "tflops": round(flop_i / (im * 1e-3) / 1e12, 2),
-                "frac_peak_bf16": round(flop_i / (im * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        rec = {"ms": round(im, 3), "tflops": round(flop_i / (im * 1e-3) / 1e12, 2),
+               "frac_peak_bf16": round(flop_i / (im * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         if do_dense:
             # output difference against the bf16 dense path on the same inputs
-            d = (out_i8.float() - out_dense.float())
-            int8["rel_diff_vs_bf16_dense"] = round(float(d.norm() / out_dense.float().norm()), 5)
-        del out_i8
+            d = (out_q.float() - out_dense.float())
+            rec["rel_diff_vs_bf16_dense"] = round(float(d.norm() / out_dense.float().norm()), 5)
+        quant[qmode] = rec
+        del out_q
+    int8 = quant.get("int8")
+    fp8 = quant.get("fp8")
 
     # the other workloads of the path, outside the step, each on its own seeded
     # inputs: 5,040 tokens x 56 heads dense in one launch; 72,576 x 16 heads
@@ -539,10 +545,11 @@ def main():
         result["vda"] = vda
     if configs is not None:
         result["configs"] = configs
-    if int8 is not None:
-        if do_dense:
-            int8["speedup_vs_dense"] = round(d_ms / int8["ms"], 3)
-        result["int8"] = int8
+    for qname, qrec in (("int8", int8), ("fp8", fp8)):
+        if qrec is not None:
+            if do_dense:
+                qrec["speedup_vs_dense"] = round(d_ms / qrec["ms"], 3)
+            result[qname] = qrec
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), budget", args.cpu_budget, "s")
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, args.cpu_budget)

@@ -13,7 +13,7 @@
  * materialized (FreeVideo page, section "Why it does not fit: the
  * arithmetic").
  *
- * Three modes:
+ * Four modes:
  *   FVATTN_DENSE         out = softmax(scale * Q K^T) V over every key.
  *   FVATTN_BLOCK_SPARSE  the sequence is cut into contiguous 128-token tiles;
  *                        tiles are mean-pooled, every query tile scores every
@@ -33,6 +33,16 @@
  *                        integer dot product).  V and P V stay bf16 as in
  *                        FVATTN_DENSE.  Uses stream-ordered scratch for the
  *                        key codes and scales (heads * tokens * 128 bytes).
+ *   FVATTN_DENSE_FP8QK   FVATTN_DENSE_INT8QK with 8-bit floating-point codes
+ *                        instead (the FP8 reading of the same page passage):
+ *                        OCP E4M3 (bias 7, 3 mantissa bits, largest finite
+ *                        448), scale = max |x| / 448 (1 for a group of zeros)
+ *                        per query row and per block of 64 consecutive keys,
+ *                        code = the E4M3 value nearest to x / scale with ties
+ *                        to the even mantissa (float32 scale and division,
+ *                        correctly rounded); score = scale * sq * sk * (dot
+ *                        product of the E4M3 values, fp32 accumulation on the
+ *                        f8f6f4 matrix cores).  Scratch as INT8.
  *
  * Selection rule, exactly (the pages leave these points open; this is the
  * library's definition): tile t covers tokens [128t, min(128t+128, N)) and has
@@ -106,7 +116,12 @@ typedef enum {
   FVATTN_ERR_HIP = 4
 } fvattn_status;
 
-typedef enum { FVATTN_DENSE = 0, FVATTN_BLOCK_SPARSE = 1, FVATTN_DENSE_INT8QK = 2 } fvattn_mode;
+typedef enum {
+  FVATTN_DENSE = 0,
+  FVATTN_BLOCK_SPARSE = 1,
+  FVATTN_DENSE_INT8QK = 2,
+  FVATTN_DENSE_FP8QK = 3
+} fvattn_mode;
 
 #define FVATTN_TILE 128       /* tokens per selection tile */
 #define FVATTN_HEAD_DIM 128   /* the only supported head width */
@@ -249,6 +264,12 @@ int fvattn_vsa_tile_count(int frames, int height, int width, int tile_t, int til
  * scales_out float [heads][ceil(tokens / 64)] out (device pointers). */
 int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
                       float* scales_out, void* stream);
+
+/* The key quantization of FVATTN_DENSE_FP8QK alone, for checking: k bf16
+ * [heads][tokens][128] in; codes_out E4M3 bytes [heads][tokens][128] and
+ * scales_out float [heads][ceil(tokens / 64)] out (device pointers). */
+int fvattn_quantize_k_fp8(const void* k, int heads, int tokens, int head_dim, uint8_t* codes_out,
+                          float* scales_out, void* stream);
 
 /* Video Delta Attention, the linear branch of Video DeltaNet (FreeVideo page,
  * section "Where Video DeltaNet comes in"), before its learned gate, norm and

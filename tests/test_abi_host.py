@@ -23,7 +23,7 @@ NULL = ctypes.c_void_p(0)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fvattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fvattn_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -284,7 +284,16 @@ def test_int8_mode_argument_checks(lib, monkeypatch):
     assert _fwd(lib, q=NULL, mode=2, frac=float("nan")) == fv.FVATTN_ERR_INVALID_ARG
     assert _fwd(lib, mode=2, hd=64) == fv.FVATTN_ERR_UNSUPPORTED
     assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0, mode=2) == fv.FVATTN_OK
-    assert _fwd(lib, mode=3) == fv.FVATTN_ERR_INVALID_ARG
+    assert _fwd(lib, mode=4) == fv.FVATTN_ERR_INVALID_ARG
+    assert _fwd(lib, mode=-1) == fv.FVATTN_ERR_INVALID_ARG
+    # mode 3 (dense, FP8 query-key scores) takes the same checks
+    assert _fwd(lib, q=NULL, mode=3, frac=float("nan")) == fv.FVATTN_ERR_INVALID_ARG
+    assert _fwd(lib, mode=3, hd=64) == fv.FVATTN_ERR_UNSUPPORTED
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, tokens=0, mode=3) == fv.FVATTN_OK
+    for qk in (lib.fvattn_quantize_k, lib.fvattn_quantize_k_fp8):
+        assert qk(NULL, 0, 100, 128, NULL, NULL, NULL) == fv.FVATTN_OK
+        assert qk(BOGUS, 2, 100, 128, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
+        assert qk(BOGUS, 2, 100, 96, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_UNSUPPORTED
     qk = lib.fvattn_quantize_k
     assert qk(NULL, 0, 100, 128, NULL, NULL, NULL) == fv.FVATTN_OK
     assert qk(BOGUS, 2, 100, 128, NULL, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
@@ -293,6 +302,7 @@ def test_int8_mode_argument_checks(lib, monkeypatch):
     assert qk(BOGUS, -2, 100, 128, BOGUS, BOGUS, NULL) == fv.FVATTN_ERR_INVALID_ARG
     monkeypatch.setenv("FVATTN_TEST_FAIL_ALLOC", "1")
     assert _fwd(lib, mode=2) == fv.FVATTN_ERR_ALLOC
+    assert _fwd(lib, mode=3) == fv.FVATTN_ERR_ALLOC
     assert lib.fvattn_forward_heads(BOGUS, BOGUS, BOGUS, BOGUS, 56, 16, 1008, 128, 0.088, 2, 0.1,
                                     NULL) == fv.FVATTN_ERR_ALLOC
 

@@ -462,6 +462,70 @@ def test_int8_head_groups_equal_one_launch_bitwise():
         assert torch.equal(whole, fv.forward_heads(q, k, v, g, mode="int8")), g
 
 
+# ------------------------------------------------------------------ FP8 (E4M3) query-key scores
+
+_E4M3 = np.array([oracle.e4m3_decode(c) for c in range(256)])
+
+
+def _fp8_values(codes):
+    """E4M3 bytes to their values (NaN codes stay NaN)."""
+    return _E4M3[codes.astype(np.int64)]
+
+
+@pytest.mark.parametrize("N,dist", [(1, "iid"), (63, "iid"), (64, "iid"), (65, "iid"), (1000, "iid"),
+                                    (5040, "frame"), (72576, "frame")])
+def test_quantize_k_fp8_bit_exact(N, dist):
+    say("quantize k fp8", N, dist)
+    _, k, _ = inputs.make_qkv(N, 2, dist, 900 + N)
+    codes, scales = fv.quantize_k_fp8(k.to(DEV))
+    codes = codes.cpu().numpy()
+    for h in range(2):
+        ref_c, ref_s = oracle.fp8.quantize_blocks(oracle.widen(k[h]))
+        assert np.array_equal(scales[h].cpu().numpy(), ref_s)
+        got = _fp8_values(codes[h])
+        assert not np.isnan(got).any()
+        assert np.array_equal(got, ref_c)
+        # the sign bit of a nonzero code is the sign of its value
+        nz = ref_c != 0
+        assert np.array_equal(codes[h][nz] >= 128, ref_c[nz] < 0)
+
+
+def test_quantize_k_fp8_rounding_edges():
+    # keys built so that k / scale lands on E4M3 midpoints (ties), subnormals
+    # and the largest magnitude 448: every 64-key block holds a 448 (scale 1)
+    vals = [448.0, 1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -9, 2.0 ** -10, 0.5 * 2.0 ** -9 * 3, 7 * 2.0 ** -9,
+            2.0 ** -6, 15.5, 240.0, 0.0, -1.0625, -448.0, 104.0, 100.0]
+    row = np.array(vals + [0.0] * (128 - len(vals)))
+    k = np.tile(row, (64, 1))
+    kt = torch.from_numpy(k.astype(np.float32)).to(torch.bfloat16).reshape(1, 64, 128)
+    assert np.array_equal(oracle.widen(kt)[0], k)                       # exact in bf16
+    codes, scales = fv.quantize_k_fp8(kt.to(DEV))
+    ref_c, ref_s = oracle.fp8.quantize_blocks(k)
+    assert np.array_equal(scales.cpu().numpy()[0], ref_s) and ref_s[0] == 1.0
+    assert np.array_equal(_fp8_values(codes.cpu().numpy()[0]), ref_c)
+
+
+@pytest.mark.parametrize("N,dist", [(1, "iid"), (5, "iid"), (64, "iid"), (65, "iid"), (129, "iid"),
+                                    (300, "iid"), (1000, "iid"), (1008, "frame"), (5040, "frame")])
+def test_fp8_attention_matches_oracle(N, dist):
+    say("fp8 attention", N, dist)
+    q, k, v = inputs.make_qkv(N, 2, dist, 950 + N)
+    out = fv.forward(*to_dev(q, k, v), mode="fp8").cpu()
+    qw, kw, vw = (oracle.widen(t) for t in (q, k, v))
+    ref = oracle.fp8_scores_attention(qw, kw, vw, 1 / math.sqrt(128))
+    assert_close(oracle.widen(out), ref, f"fp8 N={N}")
+    dense = oracle.dense(qw, kw, vw, 1 / math.sqrt(128))
+    say(f"fp8 N={N}: relative error against exact dense "
+        f"{np.linalg.norm(oracle.widen(out) - dense) / np.linalg.norm(dense):.4f}")
+
+
+def test_fp8_head_groups_equal_one_launch_bitwise():
+    q, k, v = to_dev(*inputs.make_qkv(1500, 12, "frame", 72))
+    whole = fv.forward(q, k, v, mode="fp8")
+    for g in (16, 8, 4):
+        assert torch.equal(whole, fv.forward_heads(q, k, v, g, mode="fp8")), g
+
+
 # ------------------------------------------------------------------ Video Delta Attention
 
 def _vda_case(frames, ft, heads, seed):
@@ -721,7 +785,7 @@ def test_vsa_near_the_tile_limit():
     assert_close(oracle.widen(out[:, rows].cpu()), ref, "vsa near the tile limit")
 
 
-@pytest.mark.parametrize("mode", ["dense", "sparse", "int8"])
+@pytest.mark.parametrize("mode", ["dense", "sparse", "int8", "fp8"])
 def test_many_heads_short_sequences(mode):
     # 96 heads of 200 tokens: a grid of many small heads with ragged tiles
     q, k, v = inputs.make_qkv(200, 96, "iid", 13)
@@ -733,8 +797,10 @@ def test_many_heads_short_sequences(mode):
         ref = oracle.dense(qw, kw, vw, scale)
     elif mode == "sparse":
         ref = oracle.sparse(qw, kw, vw, scale, oracle.select_tiles(qw, kw, 0.5))
-    else:
+    elif mode == "int8":
         ref = oracle.int8_scores_attention(qw, kw, vw, scale)
+    else:
+        ref = oracle.fp8_scores_attention(qw, kw, vw, scale)
     assert_close(oracle.widen(out[heads]), ref, f"{mode} 96 heads x 200")
 
 
@@ -751,6 +817,22 @@ def test_config4_int8(cfg4):
     assert_close(oracle.widen(got), ref, f"{c.name} int8")
     dense = oracle.dense(qw, kw, vw, c.scale, rows=rows)
     say(f"{c.name} int8: relative error against exact dense "
+        f"{np.linalg.norm(oracle.widen(got) - dense) / np.linalg.norm(dense):.4f}")
+
+
+@pytest.mark.timeout(400)
+def test_config4_fp8(cfg4):
+    c = inputs.CONFIGS[4]
+    q, k, v = cfg4
+    out = fv.forward_heads(*to_dev(q, k, v), c.group, scale=c.scale, mode="fp8")
+    rows = sample_rows(c.tokens, 24, 22)
+    heads = list(range(0, c.heads, 5)) + [c.heads - 1]
+    got = out[heads][:, rows].cpu()
+    qw, kw, vw = (oracle.widen(t[heads]) for t in (q, k, v))
+    ref = oracle.fp8_scores_attention(qw, kw, vw, c.scale, rows=rows)
+    assert_close(oracle.widen(got), ref, f"{c.name} fp8")
+    dense = oracle.dense(qw, kw, vw, c.scale, rows=rows)
+    say(f"{c.name} fp8: relative error against exact dense "
         f"{np.linalg.norm(oracle.widen(got) - dense) / np.linalg.norm(dense):.4f}")
 
 

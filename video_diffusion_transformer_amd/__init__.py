@@ -24,6 +24,7 @@ FVATTN_ERR_HIP = 4
 FVATTN_DENSE = 0
 FVATTN_BLOCK_SPARSE = 1
 FVATTN_DENSE_INT8QK = 2
+FVATTN_DENSE_FP8QK = 3
 TILE = 128
 HEAD_DIM = 128
 MAX_TILES = 2048
@@ -32,8 +33,9 @@ PROBE_WAVES = 4096
 PROBE_FLOP_PER_ITER = PROBE_WAVES * 4 * 32768
 
 _MODES = {"dense": FVATTN_DENSE, "sparse": FVATTN_BLOCK_SPARSE, "int8": FVATTN_DENSE_INT8QK,
+          "fp8": FVATTN_DENSE_FP8QK,
           FVATTN_DENSE: FVATTN_DENSE, FVATTN_BLOCK_SPARSE: FVATTN_BLOCK_SPARSE,
-          FVATTN_DENSE_INT8QK: FVATTN_DENSE_INT8QK}
+          FVATTN_DENSE_INT8QK: FVATTN_DENSE_INT8QK, FVATTN_DENSE_FP8QK: FVATTN_DENSE_FP8QK}
 
 _lib = None
 
@@ -54,6 +56,7 @@ SIGNATURES = {
     "fvattn_vsa_select": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _D, _P, _P]),
     "fvattn_vsa_tile_count": (_I, [_I, _I, _I, _I, _I, _I]),
     "fvattn_quantize_k": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "fvattn_quantize_k_fp8": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "fvattn_vda_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fvattn_vda_states": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "fvattn_mfma_probe": (_I, [_P, _I, _I, _P]),
@@ -318,6 +321,17 @@ def quantize_k(k, stream=None):
     scales = torch.empty((H, -(-N // 64)), dtype=torch.float32, device=k.device)
     with torch.cuda.device(k.device):
         _check(load().fvattn_quantize_k(_ptr(k), H, N, d, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
+    return codes, scales
+
+
+def quantize_k_fp8(k, stream=None):
+    """fvattn_quantize_k_fp8: (E4M3 codes uint8 [heads, tokens, 128], scales float32 [heads, ceil(tokens/64)])."""
+    torch = _torch()
+    H, N, d = _check_qkv(k)
+    codes = torch.empty((H, N, d), dtype=torch.uint8, device=k.device)
+    scales = torch.empty((H, -(-N // 64)), dtype=torch.float32, device=k.device)
+    with torch.cuda.device(k.device):
+        _check(load().fvattn_quantize_k_fp8(_ptr(k), H, N, d, _ptr(codes), _ptr(scales), _stream_ptr(stream)))
     return codes, scales
 
 

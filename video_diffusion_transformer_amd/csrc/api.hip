@@ -185,9 +185,10 @@ int run_selection(const uint16_t* q, const uint16_t* k, int heads, int tokens, i
   return hip_status(e);
 }
 
-// INT8 keys of one call: codes [H][N][128] int8 and block scales [H][ceil(N/64)].
-int forward_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int heads,
-                 int tokens, float scale, hipStream_t stream) {
+// INT8 or FP8 keys of one call: codes [H][N][128] (1 byte each) and block
+// scales [H][ceil(N/64)], then the attention with 8-bit scores.
+int forward_q8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int heads,
+               int tokens, float scale, bool fp8, hipStream_t stream) {
   const int nblk = (tokens + 63) / 64;
   const size_t codeb = align256((size_t)heads * tokens * kHeadDim);
   const size_t scaleb = align256(sizeof(float) * (size_t)heads * nblk);
@@ -196,11 +197,12 @@ int forward_int8(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16
   if (ra != FVATTN_OK) return ra;
   uint8_t* codes = (uint8_t*)base;
   float* scales = (float*)((char*)base + codeb);
-  hipError_t e = fvattn::launch_quantize_k(k, codes, scales, heads, tokens, stream);
+  hipError_t e = fvattn::launch_quantize_k(k, codes, scales, heads, tokens, fp8, stream);
   if (e == hipSuccess) {
     fvattn::ListParams lp;
     lp.kscale = scales;
-    e = fvattn::launch_attention_int8(q, codes, v, out, lp, heads, tokens, scale, stream);
+    e = fp8 ? fvattn::launch_attention_fp8(q, codes, v, out, lp, heads, tokens, scale, stream)
+            : fvattn::launch_attention_int8(q, codes, v, out, lp, heads, tokens, scale, stream);
   }
   const int rc = hip_status(e);
   const int rf = hip_status(hipFreeAsync(base, stream));
@@ -212,7 +214,8 @@ int forward_one(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_
                 int tokens, float scale, int mode, double keep_frac, hipStream_t stream) {
   if (mode == FVATTN_DENSE)
     return hip_status(fvattn::launch_attention(q, k, v, out, nullptr, 0, heads, tokens, scale, stream));
-  if (mode == FVATTN_DENSE_INT8QK) return forward_int8(q, k, v, out, heads, tokens, scale, stream);
+  if (mode == FVATTN_DENSE_INT8QK || mode == FVATTN_DENSE_FP8QK)
+    return forward_q8(q, k, v, out, heads, tokens, scale, mode == FVATTN_DENSE_FP8QK, stream);
   const int T = tiles_of(tokens);
   const int keep = keep_of(T, keep_frac);
   SparseScratch s;
@@ -231,7 +234,8 @@ int check_forward_args(const void* q, const void* k, const void* v, const void* 
                        int tokens, int head_dim, float scale, int mode, double keep_frac,
                        bool* empty) {
   *empty = false;
-  if (mode != FVATTN_DENSE && mode != FVATTN_BLOCK_SPARSE && mode != FVATTN_DENSE_INT8QK)
+  if (mode != FVATTN_DENSE && mode != FVATTN_BLOCK_SPARSE && mode != FVATTN_DENSE_INT8QK &&
+      mode != FVATTN_DENSE_FP8QK)
     return FVATTN_ERR_INVALID_ARG;
   if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FVATTN_ERR_INVALID_ARG;
@@ -514,8 +518,8 @@ int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles,
   return rc != FVATTN_OK ? rc : rf;
 }
 
-int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
-                      float* scales_out, void* stream) {
+static int quantize_k_entry(const void* k, int heads, int tokens, int head_dim, void* codes_out,
+                     float* scales_out, bool fp8, void* stream) {
   if (heads < 0 || tokens < 0) return FVATTN_ERR_INVALID_ARG;
   if (head_dim != kHeadDim) return FVATTN_ERR_UNSUPPORTED;
   if (heads == 0 || tokens == 0) return FVATTN_OK;
@@ -524,7 +528,17 @@ int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
   return hip_status(fvattn::launch_quantize_k((const uint16_t*)k, (uint8_t*)codes_out, scales_out,
-                                              heads, tokens, (hipStream_t)stream));
+                                              heads, tokens, fp8, (hipStream_t)stream));
+}
+
+int fvattn_quantize_k(const void* k, int heads, int tokens, int head_dim, int8_t* codes_out,
+                      float* scales_out, void* stream) {
+  return quantize_k_entry(k, heads, tokens, head_dim, codes_out, scales_out, false, stream);
+}
+
+int fvattn_quantize_k_fp8(const void* k, int heads, int tokens, int head_dim, uint8_t* codes_out,
+                          float* scales_out, void* stream) {
+  return quantize_k_entry(k, heads, tokens, head_dim, codes_out, scales_out, true, stream);
 }
 
 int fvattn_vda_states(const void* k, const void* v, const float* beta, const float* alpha,

@@ -1,7 +1,7 @@
 // Fused attention forward for gfx950 (MI355X): dense, restricted to a list of
 // 128-token key tiles per 128-token query tile (block-sparse), restricted to a
 // frame window (Video DeltaNet's softmax branch), over VSA-H3's packed 3D-tile
-// layout, or dense with INT8 query-key scores.
+// layout, or dense with INT8 or FP8 (E4M3) query-key scores.
 //
 // What it computes: out = softmax(scale * Q K^T) V per head, non-causal, the
 // softmax taken over every key (dense), over the keys of the listed tiles only
@@ -64,6 +64,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -147,7 +148,9 @@ using Buf = std::integral_constant<int, B>;
 // VSA-H3 per-head lists of 64-key sub-tiles over the padded tile layout (Q
 // gathered from and O scattered to the packed token order), 4 dense with INT8
 // query-key scores (K as int8 codes with per-64-key-block scales, Q quantized
-// per row here; S^T on v_mfma_i32_32x32x32_i8, PV unchanged in bf16).
+// per row here; S^T on v_mfma_i32_32x32x32_i8, PV unchanged in bf16), 5 dense
+// with FP8 (OCP E4M3) query-key scores (as 4, with E4M3 codes and S^T on the
+// f8f6f4 matrix cores, v_mfma_scale_f32_32x32x64_f8f6f4, fp32 accumulation).
 template <int kMode, int kWaves, int kStages, int kQB, int kBN>
 __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                                               const uint16_t* __restrict__ K,
@@ -155,17 +158,19 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
                                               const int32_t* __restrict__ idx, int keep, int N,
                                               int qtiles, float c, ListParams wp) {
   constexpr bool kI8 = kMode == 4;
-  constexpr bool kDenseWalk = kMode == 0 || kMode == 4;   // every key, no list
+  constexpr bool kF8 = kMode == 5;
+  constexpr bool kQ8 = kI8 || kF8;                         // 8-bit Q and K codes
+  constexpr bool kDenseWalk = kMode == 0 || kQ8;           // every key, no list
   constexpr int kKB = kBN / 32;               // 32-key MFMA blocks per stage
   constexpr int kTileBytes = kBN * kRowBytes; // one V (or bf16 K) stage
-  constexpr int kKRowBytes = kI8 ? kHeadDim : kRowBytes;      // K row in LDS: int8 or bf16
+  constexpr int kKRowBytes = kQ8 ? kHeadDim : kRowBytes;      // K row in LDS: 8-bit or bf16
   constexpr int kKTileBytes = kBN * kKRowBytes;
-  constexpr int kDK = kI8 ? 4 : 8;            // MFMAs along the head dimension
+  constexpr int kDK = kI8 ? 4 : (kF8 ? 2 : 8);   // MFMAs along the head dimension
   constexpr int kBM = 32 * kQB * kWaves;
   constexpr int kLoadsPerWave = kTileBytes / (1024 * kWaves);  // 1 KiB per wave-wide load
   constexpr int kKLoadsPerWave = kKTileBytes / (1024 * kWaves);
   static_assert(kKLoadsPerWave >= 1, "one wave-wide K load per wave at least");
-  static_assert(!kI8 || (kBN == 64 && kStages == 2), "INT8 scales are per 64-key stage, loaded one stage ahead");
+  static_assert(!kQ8 || (kBN == 64 && kStages == 2), "8-bit key scales are per 64-key stage, loaded one stage ahead");
   constexpr int kPrefetch = kStages - 1;
   static_assert(kMode != 1 || kBM == kTile, "per-head lists cover one selection tile");
   static_assert(kMode != 3 || (kBN == 64 && kBM == kVsaRows),
@@ -188,7 +193,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const size_t hoff = (size_t)h * (size_t)N * kHeadDim;
-  const unsigned char* Kh = (const unsigned char*)K + (size_t)h * N * kHeadDim * (kI8 ? 1 : 2);
+  const unsigned char* Kh = (const unsigned char*)K + (size_t)h * N * kHeadDim * (kQ8 ? 1 : 2);
   const uint16_t* Vh = V + hoff;
   // VSA: N counts padded slots; Q and O keep the packed token order
   const int qn = kMode == 3 ? wp.vsa.tokens : N;
@@ -199,6 +204,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   const int q0 = qt * kBM + wave * 32 * kQB;
   bf16x8 qf[kQB][8];
   i32x4 qf8[kQB][4];   // INT8 mode: codes of Q^T, 16 dims per lane per 32-dim block
+  i32x8 qff[kQB][2];   // FP8 mode: E4M3 codes of Q^T, 32 dims per lane per 64-dim block
   float crow[kQB];     // INT8 mode: scale * log2(e) * (this row's query scale)
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) crow[qb] = c;
@@ -242,6 +248,46 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
           codes[wd] = (int)word;
         }
         qf8[qb][dk] = codes;
+      }
+    }
+  } else if constexpr (kF8) {
+    // lane (row l32, half g) holds dims 64 dk + 32 g + 0..31 of its row; the
+    // row's scale is max |q| / 448 over both halves; E4M3 codes nearest to
+    // q / scale (correctly rounded float32 division, hardware conversion with
+    // ties to even); rows past N read zeros
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(Q + hoff + (size_t)q0 * kHeadDim, N - q0, kRowBytes);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      u32x4 w[8];
+      float m = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        w[x] = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, (32 * qb + l32) * kRowBytes + 128 * (x >> 2) + 64 * g + 16 * (x & 3), 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t u = w[x][e >> 1];
+          m = fmaxf(m, fabsf(__uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16))));
+        }
+      }
+      m = halfwave_max(m);
+      const float sq = m == 0.f ? 1.f : __fdiv_rn(m, 448.f);
+      crow[qb] = c * sq;
+      auto val = [&](int dk, int i) {   // dim 64 dk + 32 g + i
+        const uint32_t u = w[4 * dk + (i >> 3)][(i & 7) >> 1];
+        return __fdiv_rn(__uint_as_float((i & 1) ? (u & 0xffff0000u) : (u << 16)), sq);
+      };
+#pragma unroll
+      for (int dk = 0; dk < 2; ++dk) {
+        i32x8 codes;
+#pragma unroll
+        for (int wd = 0; wd < 8; ++wd) {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(val(dk, 4 * wd), val(dk, 4 * wd + 1), 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(val(dk, 4 * wd + 2), val(dk, 4 * wd + 3), word, true);
+          codes[wd] = word;
+        }
+        qff[qb][dk] = codes;
       }
     }
   } else if constexpr (kMode == 3) {
@@ -311,7 +357,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   int koffg[kKLoadsPerWave], voffg[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kKLoadsPerWave; ++i) {
-    if constexpr (kI8) {   // 8 rows of 128 B per wave-wide load
+    if constexpr (kQ8) {   // 8 rows of 128 B per wave-wide load
       const int row = 8 * (kKLoadsPerWave * wave + i) + (lane >> 3), slot = lane & 7;
       koffg[i] = row * kKRowBytes + ((slot ^ k8_swz(row)) << 4);
     } else {
@@ -340,13 +386,21 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   };
 
   // S^T operand: row key_of_row(l32) (+32 for the second 32-key block), chunk
-  // 2 dk + g; byte offsets within a stage, one per dk.
-  int koff[kDK];
+  // 2 dk + g; byte offsets within a stage, one per dk.  FP8 mode: 32 bytes per
+  // lane, chunks 4 dk + 2 g and 4 dk + 2 g + 1 (koff, koff2).
+  int koff[kDK], koff2[kDK];
   {
     const int krow = key_of_row(l32);
 #pragma unroll
-    for (int dk = 0; dk < kDK; ++dk)
-      koff[dk] = krow * kKRowBytes + (((2 * dk + g) ^ (kI8 ? k8_swz(krow) : k_swz(krow))) << 4);
+    for (int dk = 0; dk < kDK; ++dk) {
+      if constexpr (kF8) {
+        koff[dk] = krow * kKRowBytes + (((4 * dk + 2 * g) ^ k8_swz(krow)) << 4);
+        koff2[dk] = krow * kKRowBytes + (((4 * dk + 2 * g + 1) ^ k8_swz(krow)) << 4);
+      } else {
+        koff[dk] = krow * kKRowBytes + (((2 * dk + g) ^ (kI8 ? k8_swz(krow) : k_swz(krow))) << 4);
+        koff2[dk] = 0;
+      }
+    }
   }
   // V^T operand by transpose load: 16-lane group G = lane >> 4 covers head
   // dims 32 db + 16 (G & 1) + 0..15 and keys 32 kb + 16 (G >> 1) + 8 s + 0..7;
@@ -394,7 +448,17 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     for (int dk = 0; dk < kDK; ++dk)
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
-        if constexpr (kI8) {
+        if constexpr (kF8) {
+          // E4M3 x E4M3 on the f8f6f4 matrix cores (format 0 on both sides,
+          // unit block scales: E8M0 127 = 2^0), fp32 accumulation
+          const i32x4 a0 = *(const i32x4*)(kb0 + koff[dk] + kb * 32 * kKRowBytes);
+          const i32x4 a1 = *(const i32x4*)(kb0 + koff2[dk] + kb * 32 * kKRowBytes);
+          const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+            S[qb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qff[qb][dk], S[qb][kb], 0, 0,
+                                                                         0, 127, 0, 127);
+        } else if constexpr (kI8) {
           // int32 scores in the float registers (bit patterns); converted after
           const i32x4 a = *(const i32x4*)(kb0 + koff[dk] + kb * 32 * kKRowBytes);
 #pragma unroll
@@ -601,14 +665,14 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
   // (loaded during stage it with a vector load, so the stage-top vmcnt wait
   // covers it).  Other modes: the multiplier is c throughout.
   const __amdgpu_buffer_rsrc_t rks =
-      make_rsrc(kI8 ? wp.kscale + (size_t)h * nsub : nullptr, kI8 ? nsub : 0, 4);
+      make_rsrc(kQ8 ? wp.kscale + (size_t)h * nsub : nullptr, kQ8 ? nsub : 0, 4);
   auto key_scale = [&](int i) -> float {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rks, 4 * i, 0, 0));
   };
   float sk_cur = 1.f, sk_next = 1.f;
   auto multipliers = [&](float sk, float (&cm)[kQB]) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) cm[qb] = kI8 ? crow[qb] * sk : c;
+    for (int qb = 0; qb < kQB; ++qb) cm[qb] = kQ8 ? crow[qb] * sk : c;
   };
   auto stage = [&](auto kc, int it, f32x16 (&Scur)[kQB][kKB], f32x16 (&Snext)[kQB][kKB]) {
     constexpr int k = decltype(kc)::value;
@@ -633,7 +697,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     if (it + kPrefetch < nsub)
       load_v(kv_of(ring[kPrefetch - 1], it + kPrefetch) & ~kMaskFlag, Buf<(k + kStages - 1) % kStages>());
     const int ahead = !kDenseWalk ? entry(it + 1 + kStages) : 0;
-    const float sk_ahead = kI8 ? key_scale(it + 2) : 1.f;
+    const float sk_ahead = kQ8 ? key_scale(it + 2) : 1.f;
     float cm_cur[kQB], cm_next[kQB];
     multipliers(sk_cur, cm_cur);
     multipliers(sk_next, cm_next);
@@ -645,11 +709,12 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     // kReadAhead operands ahead.
     {
       constexpr int kOps = kDK * kKB, kValuPerMfma = (56 * kKB * kQB + kOps * kQB - 1) / (kOps * kQB);
+      constexpr int kReads = kF8 ? 2 : 1;   // LDS reads per K operand
 #pragma unroll
-      for (int o = 0; o < kReadAhead; ++o) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int o = 0; o < kReadAhead; ++o) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
       for (int o = 0; o < kOps; ++o) {
-        if (o + kReadAhead < kOps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (o + kReadAhead < kOps) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -711,7 +776,7 @@ __device__ __forceinline__ void attn_fwd_body(const uint16_t* __restrict__ Q,
     if (kStages > 2 && 2 < nsub) load_k(kv_of(ring[1], 2) & ~kMaskFlag, Buf<2 % kStages>());
     load_v(kv0, Buf<0>());
     if (kStages > 2 && 1 < nsub) load_v(kv1, Buf<1 % kStages>());
-    if constexpr (kI8) {
+    if constexpr (kQ8) {
       sk_cur = key_scale(0);
       sk_next = key_scale(1);
     }
@@ -842,6 +907,19 @@ hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uin
   const long long blocks = (long long)heads * qtiles;
   if (blocks <= 0) return hipSuccess;
   attn_fwd_kernel<4, 8, 2, 1, 64><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(
+      q, (const uint16_t*)kq, v, out, nullptr, 0, tokens, qtiles, c, lp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_fp8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
+                                uint16_t* out, const ListParams& lp, int heads, int tokens,
+                                float scale, hipStream_t stream) {
+  // 128 query rows per workgroup (4 waves), two workgroups per CU, as dense
+  const float c = scale * 1.4426950408889634f;  // scale * log2(e)
+  const int qtiles = (tokens + 127) / 128;
+  const long long blocks = (long long)heads * qtiles;
+  if (blocks <= 0) return hipSuccess;
+  attn_fwd_kernel<5, 4, 2, 1, 64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
       q, (const uint16_t*)kq, v, out, nullptr, 0, tokens, qtiles, c, lp);
   return hipGetLastError();
 }

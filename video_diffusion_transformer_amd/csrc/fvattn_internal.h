@@ -157,16 +157,23 @@ hipError_t launch_attention_vsa(const uint16_t* q, const uint16_t* kp, const uin
                                 uint16_t* out, const int32_t* lists, const ListParams& lp,
                                 int heads, float scale, hipStream_t stream);
 
-// INT8 keys: codes [heads][tokens][128] int8 and per-64-key-block scales
-// [heads][ceil(tokens / 64)] float.
+// INT8 (or, with fp8, OCP E4M3) keys: codes [heads][tokens][128] bytes and
+// per-64-key-block scales [heads][ceil(tokens / 64)] float.
 hipError_t launch_quantize_k(const uint16_t* k, uint8_t* codes, float* scales, int heads,
-                             int tokens, hipStream_t stream);
+                             int tokens, bool fp8, hipStream_t stream);
 
 // Dense attention with INT8 query-key scores: kq = codes from launch_quantize_k
 // (lp.kscale = their scales); queries are quantized per row in the kernel.
 hipError_t launch_attention_int8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
                                  uint16_t* out, const ListParams& lp, int heads, int tokens,
                                  float scale, hipStream_t stream);
+
+// Dense attention with FP8 (E4M3) query-key scores: kq = E4M3 codes from
+// launch_quantize_k with fp8 (lp.kscale = their scales); queries are
+// quantized per row in the kernel.
+hipError_t launch_attention_fp8(const uint16_t* q, const uint8_t* kq, const uint16_t* v,
+                                uint16_t* out, const ListParams& lp, int heads, int tokens,
+                                float scale, hipStream_t stream);
 
 // Video Delta Attention: forward and reverse states [heads][frames + 1][128][128]
 // (fp32) from k, v (bf16 [heads][frames * ft][128]), beta [heads][frames * ft],

@@ -9,6 +9,11 @@
 // correctly rounded float32 operations.  Codes are written row-major, 128 bytes
 // per key ([heads][tokens][128] int8), scales as float [heads][ceil(tokens/64)].
 // Queries are quantized per row inside the attention kernel.
+//
+// The FP8 variant (quantize_k_kernel<true>) writes OCP E4M3 codes instead:
+// scale = max |k| / 448, code = the E4M3 value nearest to k / scale (ties to
+// the even mantissa) by the hardware conversion v_cvt_pk_fp8_f32, again with a
+// correctly rounded float32 scale and division.
 
 #include "fvattn_internal.h"
 
@@ -30,6 +35,14 @@ __device__ __forceinline__ uint32_t code_byte(float x, float s) {
   return (uint32_t)((int)q & 0xff);
 }
 
+// Four FP8 E4M3 codes of x[0..3] / s packed little-endian into one word.
+__device__ __forceinline__ uint32_t fp8_word(float x0, float x1, float x2, float x3, float s) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x0, s), __fdiv_rn(x1, s), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x2, s), __fdiv_rn(x3, s), w, true);
+  return (uint32_t)w;
+}
+
+template <bool kFp8>
 __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restrict__ K,
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ scales, int N,
@@ -54,7 +67,7 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float s = m == 0.f ? 1.f : __fdiv_rn(m, 127.f);
+  const float s = m == 0.f ? 1.f : __fdiv_rn(m, kFp8 ? 448.f : 127.f);
   if (tid == 0) scales[(size_t)h * nblk + b] = s;
   if (!live) return;
   u32x4 out[2];
@@ -63,8 +76,13 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t word = 0;
+      if constexpr (kFp8) {
+        word = fp8_word(bf16_at(w[c], 4 * j), bf16_at(w[c], 4 * j + 1), bf16_at(w[c], 4 * j + 2),
+                        bf16_at(w[c], 4 * j + 3), s);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) word |= code_byte(bf16_at(w[c], 4 * j + e), s) << (8 * e);
+        for (int e = 0; e < 4; ++e) word |= code_byte(bf16_at(w[c], 4 * j + e), s) << (8 * e);
+      }
       out[c >> 1][2 * (c & 1) + j] = word;
     }
   uint8_t* o = codes + ((size_t)h * N + row) * kHeadDim + 32 * part;
@@ -75,11 +93,15 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
 }  // namespace
 
 hipError_t launch_quantize_k(const uint16_t* k, uint8_t* codes, float* scales, int heads,
-                             int tokens, hipStream_t stream) {
+                             int tokens, bool fp8, hipStream_t stream) {
   const int nblk = (tokens + kQuantBlock - 1) / kQuantBlock;
   if (heads <= 0 || nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_k_kernel, dim3(nblk, heads), dim3(256), 0, stream, k, codes, scales,
-                     tokens, nblk);
+  if (fp8)
+    hipLaunchKernelGGL(quantize_k_kernel<true>, dim3(nblk, heads), dim3(256), 0, stream, k, codes,
+                       scales, tokens, nblk);
+  else
+    hipLaunchKernelGGL(quantize_k_kernel<false>, dim3(nblk, heads), dim3(256), 0, stream, k, codes,
+                       scales, tokens, nblk);
   return hipGetLastError();
 }
 
