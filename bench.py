@@ -142,7 +142,7 @@ def main():
                                        "roofline", "configs"],
                     default=None,
                     help="time only one mode (for profiler runs; value then covers that mode, "
-                         "0 for window, vsa, int8, vda and roofline, which are timed outside the step)")
+                         "0 for window, vsa, int8, fp8, vda, configs and roofline, which are timed outside the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration runs)")
     args = ap.parse_args()
