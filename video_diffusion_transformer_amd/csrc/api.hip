@@ -112,12 +112,11 @@ int scratch_malloc(void** p, size_t bytes, hipStream_t stream) {
   return FVATTN_OK;
 }
 
-// Scratch of one sparse call: tile means of Q [H][T][128], transposed tile
-// means of K [H][128][T], the tile scores [H][T][T], and the kept tile lists
-// [H][T][keep].
+// Scratch of one sparse call: transposed tile means of Q and of K
+// [H][128][T], the tile scores [H][T][T], and the kept tile lists [H][T][keep].
 struct SparseScratch {
   void* base = nullptr;
-  double* qm = nullptr;
+  double* qmT = nullptr;
   double* kmT = nullptr;
   double* scores = nullptr;
   int32_t* idx = nullptr;
@@ -137,7 +136,7 @@ void sparse_scratch_carve(SparseScratch* s, void* base, int heads, int tiles, bo
   const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
   const size_t scoreb = align256(sizeof(double) * (size_t)heads * tiles * tiles);
   char* p = (char*)base;
-  s->qm = (double*)p;
+  s->qmT = (double*)p;
   s->kmT = (double*)(p + means);
   s->scores = (double*)(p + 2 * means);
   s->idx = need_idx ? (int32_t*)(p + 2 * means + scoreb) : nullptr;
@@ -178,9 +177,8 @@ int scratch_free(SparseScratch* s, hipStream_t stream) {
 int run_selection(const uint16_t* q, const uint16_t* k, int heads, int tokens, int keep,
                   const SparseScratch& s, int32_t* idx, hipStream_t stream) {
   const int T = tiles_of(tokens);
-  hipError_t e = fvattn::launch_tile_means(q, s.qm, heads, tokens, false, stream);
-  if (e == hipSuccess) e = fvattn::launch_tile_means(k, s.kmT, heads, tokens, true, stream);
-  if (e == hipSuccess) e = fvattn::launch_scores(s.qm, s.kmT, heads, T, s.scores, stream);
+  hipError_t e = fvattn::launch_tile_means_qk(q, k, s.qmT, s.kmT, heads, tokens, stream);
+  if (e == hipSuccess) e = fvattn::launch_scores(s.qmT, s.kmT, heads, T, s.scores, stream);
   if (e == hipSuccess) e = fvattn::launch_select(s.scores, heads, T, keep, idx, stream);
   return hip_status(e);
 }
@@ -492,7 +490,7 @@ int fvattn_tile_means(const void* x, int heads, int tokens, int head_dim, double
   if ((long long)tokens * kHeadDim > kMaxPerHead) return FVATTN_ERR_UNSUPPORTED;
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
-  return hip_status(fvattn::launch_tile_means((const uint16_t*)x, means_out, heads, tokens, false,
+  return hip_status(fvattn::launch_tile_means((const uint16_t*)x, means_out, heads, tokens,
                                               (hipStream_t)stream));
 }
 
@@ -507,14 +505,17 @@ int fvattn_tile_scores(const double* qm, const double* km, int heads, int tiles,
   int rc = check_device();
   if (rc != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  void* kmT = nullptr;
-  rc = scratch_malloc(&kmT, sizeof(double) * (size_t)heads * tiles * kHeadDim, st);
+  const size_t means = align256(sizeof(double) * (size_t)heads * tiles * kHeadDim);
+  void* base = nullptr;
+  rc = scratch_malloc(&base, 2 * means, st);
   if (rc != FVATTN_OK) return rc;
-  hipError_t e = fvattn::launch_transpose_means(km, (double*)kmT, heads, tiles, st);
-  if (e == hipSuccess)
-    e = fvattn::launch_scores(qm, (const double*)kmT, heads, tiles, scores_out, st);
+  double* qmT = (double*)base;
+  double* kmT = (double*)((char*)base + means);
+  hipError_t e = fvattn::launch_transpose_means(qm, qmT, heads, tiles, st);
+  if (e == hipSuccess) e = fvattn::launch_transpose_means(km, kmT, heads, tiles, st);
+  if (e == hipSuccess) e = fvattn::launch_scores(qmT, kmT, heads, tiles, scores_out, st);
   rc = hip_status(e);
-  const int rf = hip_status(hipFreeAsync(kmT, st));
+  const int rf = hip_status(hipFreeAsync(base, st));
   return rc != FVATTN_OK ? rc : rf;
 }
 
@@ -623,12 +624,12 @@ int fvattn_vsa_select(const void* q, const void* k, int heads, int tokens, int h
   void* base = nullptr;
   rc = scratch_malloc(&base, 2 * means + scoreb, st);
   if (rc != FVATTN_OK) return rc;
-  double* qm = (double*)base;
+  double* qmT = (double*)base;
   double* kmT = (double*)((char*)base + means);
   double* scores = (double*)((char*)base + 2 * means);
-  hipError_t e = fvattn::launch_vsa_means((const uint16_t*)q, qm, g, heads, false, st);
-  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)k, kmT, g, heads, true, st);
-  if (e == hipSuccess) e = fvattn::launch_scores(qm, kmT, heads, g.tiles, scores, st);
+  hipError_t e = fvattn::launch_vsa_means((const uint16_t*)q, (const uint16_t*)k, qmT, kmT, g,
+                                          heads, st);
+  if (e == hipSuccess) e = fvattn::launch_scores(qmT, kmT, heads, g.tiles, scores, st);
   if (e == hipSuccess) e = fvattn::launch_select(scores, heads, g.tiles, keep, idx_out, st);
   rc = hip_status(e);
   const int rf = hip_status(hipFreeAsync(base, st));
@@ -664,16 +665,16 @@ int fvattn_forward_vsa(const void* q, const void* k, const void* v, void* out, i
   char* p = (char*)base;
   uint16_t* kp = (uint16_t*)p;
   uint16_t* vp = (uint16_t*)(p + packed);
-  double* qm = (double*)(p + 2 * packed);
+  double* qmT = (double*)(p + 2 * packed);
   double* kmT = (double*)(p + 2 * packed + means);
   int32_t* idx = (int32_t*)(p + 2 * packed + 2 * means);
   int32_t* lists = (int32_t*)(p + 2 * packed + 2 * means + idxb);
   int32_t* counts = (int32_t*)(p + 2 * packed + 2 * means + idxb + listb);
   double* scores = (double*)(p + 2 * packed + 2 * means + idxb + listb + cntb);
   hipError_t e = fvattn::launch_vsa_pack((const uint16_t*)k, (const uint16_t*)v, kp, vp, g, heads, st);
-  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)q, qm, g, heads, false, st);
-  if (e == hipSuccess) e = fvattn::launch_vsa_means((const uint16_t*)k, kmT, g, heads, true, st);
-  if (e == hipSuccess) e = fvattn::launch_scores(qm, kmT, heads, g.tiles, scores, st);
+  if (e == hipSuccess)
+    e = fvattn::launch_vsa_means((const uint16_t*)q, (const uint16_t*)k, qmT, kmT, g, heads, st);
+  if (e == hipSuccess) e = fvattn::launch_scores(qmT, kmT, heads, g.tiles, scores, st);
   if (e == hipSuccess) e = fvattn::launch_select(scores, heads, g.tiles, keep, idx, st);
   if (e == hipSuccess) e = fvattn::launch_vsa_lists(idx, keep, g, heads, lists, counts, st);
   if (e == hipSuccess) {

@@ -138,11 +138,10 @@ hipError_t launch_window_tiles(int tokens, const ListParams& wp, int q_rows, boo
 hipError_t launch_vsa_pack(const uint16_t* k, const uint16_t* v, uint16_t* kp, uint16_t* vp,
                            const VsaGeom& g, int heads, hipStream_t stream);
 
-// VSA-H3: fp64 means of every video tile of x (original layout), summed in the
-// tile's token order: out [heads][tiles][128], or [heads][128][tiles] when
-// transposed.
-hipError_t launch_vsa_means(const uint16_t* x, double* out, const VsaGeom& g, int heads,
-                            bool transposed, hipStream_t stream);
+// VSA-H3: fp64 means of every video tile of q and of k (original layout),
+// summed in the tile's token order, in one launch: qmT, kmT [heads][128][tiles].
+hipError_t launch_vsa_means(const uint16_t* q, const uint16_t* k, double* qmT, double* kmT,
+                            const VsaGeom& g, int heads, hipStream_t stream);
 
 // VSA-H3: per (head, kVsaRows-row query block) the ascending list of 64-key
 // sub-tiles its rows attend to, from the kept video tiles idx [heads][tiles][keep]:
@@ -188,14 +187,18 @@ hipError_t launch_vda_states(const uint16_t* k, const uint16_t* v, const float* 
 hipError_t launch_vda_readout(const uint16_t* q, const float* fwd, const float* rev, int heads,
                               int frames, int ft, int chunk, int nb, float* out, hipStream_t stream);
 
-// S1: fp64 tile means.  transposed == false: out [heads][T][128];
-// transposed == true: out [heads][128][T].
+// S1: fp64 tile means out [heads][T][128].
 hipError_t launch_tile_means(const uint16_t* x, double* out, int heads, int tokens,
-                             bool transposed, hipStream_t stream);
+                             hipStream_t stream);
 
-// S2: canonical fp64 scores of qm [heads][T][128] against kmT [heads][128][T]
-// into scores_out [heads][T][T].
-hipError_t launch_scores(const double* qm, const double* kmT, int heads, int tiles,
+// S1 for one selection: query and key means in one launch, both transposed:
+// qmT, kmT [heads][128][T].
+hipError_t launch_tile_means_qk(const uint16_t* q, const uint16_t* k, double* qmT, double* kmT,
+                                int heads, int tokens, hipStream_t stream);
+
+// S2: canonical fp64 scores of qmT against kmT (both [heads][128][T]) into
+// scores_out [heads][T][T].
+hipError_t launch_scores(const double* qmT, const double* kmT, int heads, int tiles,
                          double* scores_out, hipStream_t stream);
 
 // S3: the top `keep` tiles of every row of scores [heads][T][T] into idx_out

@@ -8,14 +8,18 @@
 //     fp64.  The sum runs in token order from +0.0 (one thread owns 8 head
 //     dimensions of one tile and adds its tokens one after another), then one
 //     IEEE-correct fp64 division by the number of valid tokens.  HBM-bound: it
-//     reads Q and K once with 128-bit loads, 16 lanes per 256-byte token row.
+//     reads Q and K once with 128-bit loads, 16 lanes per 256-byte token row,
+//     Q and K in one launch, both written transposed for S2.
 // S2  scores_kernel: sigma_ij = sum_d qm_i[d] * km_j[d] in fp64 from +0.0 in
 //     order d = 0..127, every product and every sum rounded on its own (fp
 //     contraction is off in this file).  A workgroup owns a 64 x 64 block of
-//     (query tile, key tile) pairs; the means pass through LDS in chunks of 32
-//     dimensions and every thread keeps a 4 x 4 block of running sums in
-//     registers, each summed in the canonical order.  The scores go to a
-//     stream-ordered scratch matrix [heads][T][T].
+//     (query tile, key tile) pairs; both mean sets arrive transposed
+//     ([heads][128][T]), so a chunk of 32 dimensions is 32 runs of 64
+//     consecutive doubles per side: coalesced loads, bank-conflict-free LDS
+//     writes, and the next chunk's loads in flight while this one is summed.
+//     Every thread keeps a 4 x 4 block of running sums in registers, each
+//     summed in the canonical order.  The scores go to a stream-ordered
+//     scratch matrix [heads][T][T].
 // S3  select_kernel: per query tile, the `keep` largest scores, ties to the
 //     lower key tile, found by one wave with a most-significant-bit-first radix
 //     select on the order-preserving 64-bit image of the doubles, then emitted
@@ -40,10 +44,9 @@ __device__ __forceinline__ double bf16_hi(uint32_t w) {
 }
 
 template <bool kTransposed>
-__global__ __launch_bounds__(256) void tile_means_kernel(const uint16_t* __restrict__ X,
-                                                         double* __restrict__ out, int N, int T) {
+__device__ __forceinline__ void tile_means_body(const uint16_t* __restrict__ X,
+                                                double* __restrict__ out, int N, int T, int h) {
   __shared__ double stage[kHeadDim * kMeansTiles];
-  const int h = blockIdx.y;
   const int tid = threadIdx.x, tt = tid >> 4, c = tid & 15;
   const int t = blockIdx.x * kMeansTiles + tt;
   double acc[8];
@@ -84,6 +87,24 @@ __global__ __launch_bounds__(256) void tile_means_kernel(const uint16_t* __restr
     const int t2 = blockIdx.x * kMeansTiles + t0 + e;
     if (t2 < T) out[((size_t)h * kHeadDim + d) * T + t2] = stage[d * kMeansTiles + t0 + e];
   }
+}
+
+// Means of one tensor, [heads][T][128] (the step-alone entry point).
+__global__ __launch_bounds__(256) void tile_means_kernel(const uint16_t* __restrict__ X,
+                                                         double* __restrict__ out, int N, int T) {
+  tile_means_body<false>(X, out, N, T, blockIdx.y);
+}
+
+// Query and key means of one selection in one launch (blockIdx.z: 0 = Q,
+// 1 = K), both transposed [heads][128][T] for the score kernel.
+__global__ __launch_bounds__(256) void tile_means_qk_kernel(const uint16_t* __restrict__ Q,
+                                                            const uint16_t* __restrict__ K,
+                                                            double* __restrict__ qmT,
+                                                            double* __restrict__ kmT, int N, int T) {
+  if (blockIdx.z == 0)
+    tile_means_body<true>(Q, qmT, N, T, blockIdx.y);
+  else
+    tile_means_body<true>(K, kmT, N, T, blockIdx.y);
 }
 
 // Order-preserving map of a double onto uint64 (larger double -> larger key).
@@ -157,31 +178,45 @@ __device__ void select_row(const double* sc, int T, int keep, int32_t* __restric
   }
 }
 
-__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qm,
+__global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qmT,
                                                      const double* __restrict__ kmT, int T,
                                                      double* __restrict__ scores) {
+  constexpr int kPer = kChunk * kBlk / 256;   // doubles per thread and side per chunk
+  static_assert(kBlk == 64 && kPer * 256 == kChunk * kBlk && kHeadDim % kChunk == 0,
+                "one 64-tile run per wave row, 4 rows per pass");
   __shared__ double qs[kChunk][kBlk];   // qs[d][i]: query means of the block, this chunk
   __shared__ double ks[kChunk][kBlk];   // ks[d][j]: key means of the block, this chunk
   const int h = blockIdx.z, i0 = blockIdx.y * kBlk, j0 = blockIdx.x * kBlk;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const double* qh = qm + (size_t)h * T * kHeadDim;
+  const double* qh = qmT + (size_t)h * kHeadDim * T;
   const double* kh = kmT + (size_t)h * kHeadDim * T;
+  // element e of this thread: dimension d0 + (tid >> 6) + 4 e, tile (tid & 63)
+  const int c = tid & 63, dr = tid >> 6;
+  const bool qok = i0 + c < T, kok = j0 + c < T;
+  double qreg[kPer], kreg[kPer];
+  auto fetch = [&](int d0) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const size_t row = (size_t)(d0 + dr + 4 * e) * T;
+      qreg[e] = qok ? qh[row + i0 + c] : 0.0;
+      kreg[e] = kok ? kh[row + j0 + c] : 0.0;
+    }
+  };
   double acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  fetch(0);
   for (int d0 = 0; d0 < kHeadDim; d0 += kChunk) {
     __syncthreads();
-    for (int x = tid; x < kChunk * kBlk; x += 256) {
-      // query means: row i0 + (x / kChunk), dimension d0 + x % kChunk (row-major reads)
-      const int r = x / kChunk, d = x - r * kChunk;
-      qs[d][r] = (i0 + r < T) ? qh[(size_t)(i0 + r) * kHeadDim + d0 + d] : 0.0;
-      // key means: dimension d0 + x / kBlk, tile j0 + x % kBlk (transposed: row-major reads)
-      const int dd = x / kBlk, c = x - dd * kBlk;
-      ks[dd][c] = (j0 + c < T) ? kh[(size_t)(d0 + dd) * T + j0 + c] : 0.0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      qs[dr + 4 * e][c] = qreg[e];
+      ks[dr + 4 * e][c] = kreg[e];
     }
     __syncthreads();
+    if (d0 + kChunk < kHeadDim) fetch(d0 + kChunk);
 #pragma unroll 4
     for (int d = 0; d < kChunk; ++d) {
       double qv[4], kv[4];
@@ -227,22 +262,28 @@ __global__ void transpose_means_kernel(const double* __restrict__ in, double* __
 }  // namespace
 
 hipError_t launch_tile_means(const uint16_t* x, double* out, int heads, int tokens,
-                             bool transposed, hipStream_t stream) {
+                             hipStream_t stream) {
   const int T = (tokens + kTile - 1) / kTile;
   if (heads <= 0 || T <= 0) return hipSuccess;
   const dim3 grid((T + kMeansTiles - 1) / kMeansTiles, heads);
-  if (transposed)
-    hipLaunchKernelGGL(tile_means_kernel<true>, grid, dim3(256), 0, stream, x, out, tokens, T);
-  else
-    hipLaunchKernelGGL(tile_means_kernel<false>, grid, dim3(256), 0, stream, x, out, tokens, T);
+  hipLaunchKernelGGL(tile_means_kernel, grid, dim3(256), 0, stream, x, out, tokens, T);
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const double* qm, const double* kmT, int heads, int tiles,
+hipError_t launch_tile_means_qk(const uint16_t* q, const uint16_t* k, double* qmT, double* kmT,
+                                int heads, int tokens, hipStream_t stream) {
+  const int T = (tokens + kTile - 1) / kTile;
+  if (heads <= 0 || T <= 0) return hipSuccess;
+  const dim3 grid((T + kMeansTiles - 1) / kMeansTiles, heads, 2);
+  hipLaunchKernelGGL(tile_means_qk_kernel, grid, dim3(256), 0, stream, q, k, qmT, kmT, tokens, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const double* qmT, const double* kmT, int heads, int tiles,
                          double* scores_out, hipStream_t stream) {
   if (heads <= 0 || tiles <= 0) return hipSuccess;
   const int nb = (tiles + kBlk - 1) / kBlk;
-  hipLaunchKernelGGL(scores_kernel, dim3(nb, nb, heads), dim3(256), 0, stream, qm, kmT, tiles,
+  hipLaunchKernelGGL(scores_kernel, dim3(nb, nb, heads), dim3(256), 0, stream, qmT, kmT, tiles,
                      scores_out);
   return hipGetLastError();
 }

@@ -9,9 +9,11 @@
 // tile becomes a run of S slots, its valid tokens first.  Here:
 // * vsa_pack_kernel: K and V into that layout (HBM copy, 16 B per lane,
 //   coalesced 256-byte rows; padding slots written as zeros).
-// * vsa_means_kernel: fp64 mean of every video tile of Q or K, read from the
-//   caller's layout; the sum walks the tile's tokens in (t, h, w) raster order
-//   from +0.0, then one correctly rounded division by the tile's token count.
+// * vsa_means_kernel: fp64 mean of every video tile of Q and of K (one launch,
+//   blockIdx.z picks the tensor), read from the caller's layout and written
+//   transposed [heads][128][tiles] for the score kernel; the sum walks the
+//   tile's tokens in (t, h, w) raster order from +0.0, then one correctly
+//   rounded division by the tile's token count.
 //   Scores and top-k then run in select.hip over the video tiles only.
 // * vsa_lists_kernel: per head and kVsaRows-row query block, the ascending list of
 //   64-key sub-tiles that some query of the block attends to: every non-empty
@@ -59,10 +61,13 @@ __global__ __launch_bounds__(256) void vsa_pack_kernel(const uint16_t* __restric
   *(u32x4*)(Vp + dst) = vw;
 }
 
-template <bool kTransposed>
-__global__ __launch_bounds__(256) void vsa_means_kernel(const uint16_t* __restrict__ X,
-                                                        double* __restrict__ out, VsaGeom g) {
+__global__ __launch_bounds__(256) void vsa_means_kernel(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ K,
+                                                        double* __restrict__ qmT,
+                                                        double* __restrict__ kmT, VsaGeom g) {
   __shared__ double stage[kHeadDim * kMeansTiles];
+  const uint16_t* const X = blockIdx.z == 0 ? Q : K;
+  double* const out = blockIdx.z == 0 ? qmT : kmT;
   const int h = blockIdx.y;
   const int tid = threadIdx.x, tl = tid >> 4, c = tid & 15;
   const int j = blockIdx.x * kMeansTiles + tl;
@@ -89,14 +94,6 @@ __global__ __launch_bounds__(256) void vsa_means_kernel(const uint16_t* __restri
     const double n = (double)(t.et * t.eh * t.ew);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = acc[e] / n;
-  }
-  if (!kTransposed) {
-    if (j < T) {
-      double* o = out + ((size_t)h * T + j) * kHeadDim + 8 * c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = acc[e];
-    }
-    return;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) stage[(8 * c + e) * kMeansTiles + tl] = acc[e];
@@ -175,14 +172,11 @@ hipError_t launch_vsa_pack(const uint16_t* k, const uint16_t* v, uint16_t* kp, u
   return hipGetLastError();
 }
 
-hipError_t launch_vsa_means(const uint16_t* x, double* out, const VsaGeom& g, int heads,
-                            bool transposed, hipStream_t stream) {
+hipError_t launch_vsa_means(const uint16_t* q, const uint16_t* k, double* qmT, double* kmT,
+                            const VsaGeom& g, int heads, hipStream_t stream) {
   if (heads <= 0 || g.tiles <= 0) return hipSuccess;
-  const dim3 grid((g.tiles + kMeansTiles - 1) / kMeansTiles, heads);
-  if (transposed)
-    hipLaunchKernelGGL(vsa_means_kernel<true>, grid, dim3(256), 0, stream, x, out, g);
-  else
-    hipLaunchKernelGGL(vsa_means_kernel<false>, grid, dim3(256), 0, stream, x, out, g);
+  const dim3 grid((g.tiles + kMeansTiles - 1) / kMeansTiles, heads, 2);
+  hipLaunchKernelGGL(vsa_means_kernel, grid, dim3(256), 0, stream, q, k, qmT, kmT, g);
   return hipGetLastError();
 }
 
