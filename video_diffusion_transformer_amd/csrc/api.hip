@@ -448,12 +448,12 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
   hipStream_t st = (hipStream_t)stream;
   const int T = tiles_of(tokens);
   const int blocks = (tokens - 1) / fvattn::kWindowRows + 1;
-  void* scratch = nullptr;
+  void* mem = nullptr;
   const size_t idx_bytes = align256(sizeof(int32_t) * (size_t)blocks * T);
-  rc = scratch_malloc(&scratch, idx_bytes + align256(sizeof(int32_t) * (size_t)blocks), st);
+  rc = scratch_malloc(&mem, idx_bytes + align256(sizeof(int32_t) * (size_t)blocks), st);
   if (rc != FVATTN_OK) return rc;
-  int32_t* idx = (int32_t*)scratch;
-  int32_t* counts = (int32_t*)((char*)scratch + idx_bytes);
+  int32_t* idx = (int32_t*)mem;
+  int32_t* counts = (int32_t*)((char*)mem + idx_bytes);
   fvattn::ListParams wp;
   wp.counts = counts;
   wp.prefix = prefix_tokens;
@@ -477,7 +477,7 @@ int fvattn_forward_window(const void* q, const void* k, const void* v, void* out
     e = fvattn::launch_attention_window((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                         (uint16_t*)out, idx, wp, heads, tokens, scale, st);
   rc = hip_status(e);
-  const int rf = hip_status(hipFreeAsync(scratch, st));
+  const int rf = hip_status(hipFreeAsync(mem, st));
   return rc != FVATTN_OK ? rc : rf;
 }
 
@@ -554,14 +554,14 @@ int fvattn_vda_states(const void* k, const void* v, const float* beta, const flo
   rc = check_device();
   if (rc != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  void* scratch = nullptr;
+  void* mem = nullptr;
   const size_t bytes = sizeof(float) * 5 * (size_t)heads * frames * kHeadDim * kHeadDim;
-  rc = scratch_malloc(&scratch, bytes, st);
+  rc = scratch_malloc(&mem, bytes, st);
   if (rc != FVATTN_OK) return rc;
   rc = hip_status(fvattn::launch_vda_states((const uint16_t*)k, (const uint16_t*)v, beta, alpha,
-                                            s_text, heads, frames, frame_tokens, (float*)scratch,
+                                            s_text, heads, frames, frame_tokens, (float*)mem,
                                             fwd_out, rev_out, st));
-  const int rf = hip_status(hipFreeAsync(scratch, st));
+  const int rf = hip_status(hipFreeAsync(mem, st));
   return rc != FVATTN_OK ? rc : rf;
 }
 
@@ -581,10 +581,10 @@ int fvattn_vda_forward(const void* q, const void* k, const void* v, const float*
   hipStream_t st = (hipStream_t)stream;
   const size_t mat = (size_t)kHeadDim * kHeadDim;
   const size_t work = 5 * (size_t)heads * frames * mat, states = (size_t)heads * (frames + 1) * mat;
-  void* scratch = nullptr;
-  rc = scratch_malloc(&scratch, sizeof(float) * (work + 2 * states), st);
+  void* mem = nullptr;
+  rc = scratch_malloc(&mem, sizeof(float) * (work + 2 * states), st);
   if (rc != FVATTN_OK) return rc;
-  float* w = (float*)scratch;
+  float* w = (float*)mem;
   float* fwd = w + work;
   float* rev = fwd + states;
   hipError_t e = fvattn::launch_vda_states((const uint16_t*)k, (const uint16_t*)v, beta, alpha,
@@ -593,7 +593,7 @@ int fvattn_vda_forward(const void* q, const void* k, const void* v, const float*
     e = fvattn::launch_vda_readout((const uint16_t*)q, fwd, rev, heads, frames, frame_tokens,
                                    chunk_frames, neighbours, out, st);
   rc = hip_status(e);
-  const int rf = hip_status(hipFreeAsync(scratch, st));
+  const int rf = hip_status(hipFreeAsync(mem, st));
   return rc != FVATTN_OK ? rc : rf;
 }
 
