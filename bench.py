@@ -417,7 +417,7 @@ def main():
                 v_ms.append(v_ev[0].elapsed_time(v_ev[1]))
         vidx = fv.vsa_select(pq, pk, prefix, grid, tile, KEEP_FRAC).cpu().numpy()
         # the frame window on the same packed sequence: the 512 non-video
-        # tokens are dense rows and columns (text and audio stay fully softmax)
+        # tokens are dense rows and columns (text and audio keep full softmax attention)
         window_prefix = None
         if do_window:
             ft = grid[1] * grid[2]

@@ -192,7 +192,7 @@ int fvattn_forward_heads(const void* q, const void* k, const void* v, void* out,
 /* Frame-window softmax, the softmax branch of Video DeltaNet (FreeVideo page,
  * section "Where Video DeltaNet comes in"): exact softmax attention over a
  * packed sequence of prefix_tokens non-video tokens (text, audio) followed by
- * the video tokens.  Text and audio interactions stay fully softmax: a
+ * the video tokens.  Text and audio tokens keep full softmax attention: a
  * non-video query sees every key and every query sees every non-video key.
  * A video query of latent frame qf sees a video key of latent frame kf only if
  * |qf / chunk_frames - kf / chunk_frames| <= neighbours (integer division;

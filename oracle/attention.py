@@ -16,8 +16,8 @@ Sources (the pages are the authority on what is computed):
   two: VSA-H3 makes each of the four calls cheaper"); scores are streamed, never
   materialized (FreeVideo page, section "Why it does not fit: the arithmetic").
   The oracle is the plain definition, softmax(scale * Q K^T) V.
-* Tile selection: a coarse pooling stage scores every tile against the query
-  tile, then ``compute_topk`` keeps max(1, min(ceil((1 - sparsity) * blocks),
+* Tile selection: pooled tile summaries give a cheap score for every (query
+  tile, key tile) pair, then ``compute_topk`` keeps max(1, min(ceil((1 - sparsity) * blocks),
   blocks)) tiles (FastH3 page, "Lever two").  The pages do not fix the pooling
   operator, the score precision or the tie rule; the readings used here are:
   mean over the valid tokens of a contiguous 128-token tile, fp64 sums in token
@@ -194,10 +194,10 @@ def sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, idx: np.nd
 # windowed softmax of Video DeltaNet's softmax branch (definition)
 #
 # FreeVideo page, section "Where Video DeltaNet comes in": softmax stays exact
-# but only inside a window; each query chunk of five latent frames sees itself
-# and its neighbouring chunk on each side (a 15-frame window); every frame also
-# sees the first and the last latent frame, and those two frames see every
-# frame.  Readings taken here: latent frame of token i = i // frame_tokens;
+# but only inside a window.  Queries are grouped in chunks of five latent
+# frames; a chunk attends to its own frames and to the adjacent chunk on either
+# side (15 frames in all).  The first and the last latent frame are visible to
+# every query, and their own queries attend to every frame.  Readings taken here: latent frame of token i = i // frame_tokens;
 # chunk of frame f = f // chunk_frames, counted from frame 0 (the last chunk
 # may be short); "neighbours" chunks on each side.
 # --------------------------------------------------------------------------
@@ -256,7 +256,7 @@ def window_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
     """Softmax attention restricted to the window and anchor frames, per head.
 
     The sequence is ``prefix`` non-video tokens (text, audio) followed by the
-    video tokens.  Text and audio interactions stay fully softmax (FreeVideo
+    video tokens.  Text and audio tokens keep full softmax attention (FreeVideo
     page, "Where Video DeltaNet comes in"): a prefix query attends to every
     key, and every query attends to every prefix key; a video query attends to
     the video keys of its window and of the anchor frames.

@@ -6,9 +6,10 @@ the HIP library and imports nothing from it.
 
 What is computed: the FastH3 page ("FastH3 Preview v1: four calls,
 one-tenth the attention...", section "Update: consumer GPUs and Trim",
-subsection "Per device", the RTX 4090 paragraph) reports that queries and keys
-are quantized to INT8 for the attention scores, about 1.6x faster at about
-0.6% relative error; the values and the P V product stay in higher precision.
+subsection "Per device", the RTX 4090 paragraph) reports 8-bit integer codes
+for the queries and keys that enter the score product, measured there at about
+1.6x the speed with about 0.6% relative error; V and the P V product keep
+higher precision.
 The page does not give the quantization granularity, rounding or scale rule;
 the readings taken here:
 

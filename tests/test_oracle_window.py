@@ -1,9 +1,9 @@
 """Pins of the windowed-softmax oracle (Video DeltaNet's softmax branch).
 
-FreeVideo page, section "Where Video DeltaNet comes in": each query chunk of
-five latent frames sees itself and its two neighbouring chunks (a 15-frame
-window); every frame sees the first and last latent frames, which see every
-frame.
+FreeVideo page, section "Where Video DeltaNet comes in": queries in a chunk of
+five latent frames attend to their own chunk and the adjacent chunk on either
+side (15 frames); the first and last latent frames are visible to every query
+and attend to every frame themselves.
 """
 
 import math
@@ -176,7 +176,7 @@ def test_attention_mutant_caught():
 
 
 # ---------------------------------------------------------------- non-video prefix
-# Text and audio tokens stay fully softmax (FreeVideo page, "Where Video
+# Text and audio tokens keep full softmax attention (FreeVideo page, "Where Video
 # DeltaNet comes in"): with P non-video tokens ahead of the video, a prefix
 # query sees every key and every query sees every prefix key.
 

@@ -6,7 +6,7 @@
 // One wave per block of q_rows query tokens (128, the tile size, for both the
 // public lists and the attention workgroups).  A key tile is listed when some query of the
 // block may attend to some key of it.  Non-video tokens (text, audio) ahead of
-// the video stay fully softmax: a block holding a prefix row lists every
+// the video keep full softmax attention: a block holding a prefix row lists every
 // tile, and a tile holding a prefix key is listed for every block.  Frames inside a tile are contiguous
 // and chunks grow with frames, so this is a closed-form interval test: either
 // tile holds an anchor frame, or the chunk ranges of the two tiles lie within
