@@ -71,11 +71,12 @@
  * Stream: `stream` is a hipStream_t passed as void*; NULL means the default
  *   stream.  Every call only enqueues work and returns; no host
  *   synchronization happens inside.
- * Graph capture: dense-mode fvattn_forward and fvattn_forward_heads and
- *   fvattn_forward_indexed allocate nothing and enqueue only kernels, so a
- *   caller can capture them into a HIP graph and replay it (after one call
- *   outside capture, which caches the device check).  The other entry points
- *   allocate stream-ordered scratch inside the call.
+ * Graph capture: dense-mode fvattn_forward and fvattn_forward_heads,
+ *   fvattn_forward_indexed and fvattn_forward_sparse_noalloc allocate nothing
+ *   and enqueue only kernels, so a caller can capture them into a HIP graph
+ *   and replay it (after one call outside capture, which caches the device
+ *   check and, for the last one, the address of its static scratch).  The
+ *   other entry points allocate stream-ordered scratch inside the call.
  * Bounds: nothing is read or written past `tokens`; a partial last tile is
  *   masked (its missing keys get -inf scores, its missing query rows are never
  *   stored).
@@ -97,7 +98,8 @@
  *     FVATTN_ERR_HIP          a HIP call or kernel launch reported an error.
  * Numerics: QK^T and PV run as bf16 matrix-core products with fp32
  *   accumulation; the online softmax keeps an fp32 running max and sum; P is
- *   rounded to bf16 before the PV product; out is rounded to bf16.
+ *   rounded to bf16 before the PV product and the running sum adds those
+ *   bf16 values; out is rounded to bf16.
  */
 #ifndef FVATTN_H
 #define FVATTN_H

@@ -250,19 +250,23 @@ def test_head_groups_equal_one_launch_bitwise():
 
 
 def test_allocation_free_paths_replay_in_a_graph():
-    # dense attention, the head-group launcher in dense mode and sparse
-    # attention from caller lists allocate nothing, so they can be captured
-    # into a graph; every replay, with eager work and synchronizations in
-    # between, must reproduce the eager result bit for bit
+    # dense attention, the head-group launcher in dense mode, sparse
+    # attention from caller lists and the block-sparse path with static
+    # scratch allocate nothing, so they can be captured into a graph; every
+    # replay, with eager work and synchronizations in between, must reproduce
+    # the eager result bit for bit
     q, k, v = to_dev(*inputs.make_qkv(1500, 6, "frame", 72))
     idx = fv.select_tiles(q, k, keep_frac=0.25)
-    want = [fv.forward(q, k, v), fv.forward_heads(q, k, v, 4), fv.forward_indexed(q, k, v, idx)]
+    want = [fv.forward(q, k, v), fv.forward_heads(q, k, v, 4), fv.forward_indexed(q, k, v, idx),
+            fv.forward_sparse_noalloc(q, k, v, keep_frac=0.25)]
+    assert torch.equal(want[3], fv.forward(q, k, v, mode="sparse", keep_frac=0.25))
     outs = [torch.empty_like(q) for _ in want]
 
     def run():
         fv.forward(q, k, v, out=outs[0])
         fv.forward_heads(q, k, v, 4, out=outs[1])
         fv.forward_indexed(q, k, v, idx, out=outs[2])
+        fv.forward_sparse_noalloc(q, k, v, keep_frac=0.25, out=outs[3])
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -280,7 +284,7 @@ def test_allocation_free_paths_replay_in_a_graph():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for name, o, w in zip(("dense", "heads", "indexed"), outs, want):
+        for name, o, w in zip(("dense", "heads", "indexed", "noalloc"), outs, want):
             assert torch.equal(o, w), (rep, name)
         del scratch
 
