@@ -113,6 +113,36 @@ def test_dense_on_side_stream_and_scale():
     assert_close(oracle.widen(out.cpu()), ref, "side stream scale 0.3")
 
 
+def test_scratch_paths_on_two_concurrent_streams():
+    # the paths that take stream-ordered scratch, enqueued alternately on two
+    # streams without synchronizing in between (their scratch lifetimes
+    # overlap in time), give bitwise the results of one sequential run
+    q, k, v = to_dev(*inputs.make_qkv(2100, 4, "frame", 17))
+    pq, pk, pv = to_dev(*inputs.make_packed_qkv(40, (4, 8, 12), 4, 18))
+    calls = [
+        lambda s: fv.forward(q, k, v, mode="sparse", keep_frac=0.2, stream=s),
+        lambda s: fv.forward_window(q, k, v, frame_tokens=100, chunk_frames=2, neighbours=1, stream=s),
+        lambda s: fv.forward(q, k, v, mode="int8", stream=s),
+        lambda s: fv.forward(q, k, v, mode="fp8", stream=s),
+        lambda s: fv.forward_vsa(pq, pk, pv, 40, (4, 8, 12), (4, 4, 4), 0.3, stream=s),
+        lambda s: fv.select_tiles(q, k, keep_frac=0.3, stream=s),
+    ]
+    want = [c(None) for c in calls]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = []
+    for rep in range(2):
+        for i, c in enumerate(calls):
+            s = streams[(i + rep) % 2]
+            with torch.cuda.stream(s):
+                got.append(c(s))
+    torch.cuda.synchronize()
+    for j, g in enumerate(got):
+        assert torch.equal(g, want[j % len(calls)]), j
+
+
 def test_dense_writes_nothing_past_the_output():
     N, H = 300, 2
     q, k, v = to_dev(*inputs.make_qkv(N, H, "iid", 11))
